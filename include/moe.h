@@ -1,0 +1,186 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer library.
+ *
+ * The layer: a router scores every token against 256 experts, keeps the 8
+ * best plus one shared expert that every token uses ("Lily: Perplexity's
+ * Custom Inference Engine for Apple Silicon", section "The architecture that
+ * forces the issue: MoE plus Gated DeltaNet"); routing histograms and block
+ * maps stay on the GPU with no host round trip, and 4-bit expert weights are
+ * rebuilt tile by tile inside the grouped GEMM, never written back expanded
+ * ("Inside Lily: How Perplexity's Rust and Metal Engine Accelerates Qwen
+ * Inference on Apple Silicon", section "Performance Gains and Workload
+ * Patterns"); prefill runs as matrix-unit GEMMs and batch-1 decode as
+ * bandwidth-bound GEMV on the vector ALUs (Lily page, section "Why Apple
+ * Silicon isn't just a smaller datacenter GPU").
+ *
+ * Conventions for every entry point:
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates no device memory and keeps no device state between calls; the
+ *     caller provides scratch memory as `workspace` where a call needs it.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue their kernels on it and return without synchronising the
+ *     host; results are ready when the stream reaches that point.
+ *   - Arguments and shapes are validated on the host before anything is
+ *     launched; a failed check returns its status and launches nothing.  A
+ *     launch failure returns MOE_ERR_HIP (see moe_last_hip_error()).
+ *   - Row-major layouts; bf16 and fp16 values are passed as uint16_t bit patterns.
+ *   - Calls that share a workspace on one stream are ordered; calls that
+ *     overlap on different streams must use different workspaces.
+ *
+ * Supported shapes: hidden % 64 == 0, inter % 32 == 0, shared_inter % 32 == 0,
+ * group_size == 64, n_experts % 16 == 0 and 16 <= n_experts <= 256,
+ * 1 <= top_k <= 16 (top_k <= n_experts), 1 <= T <= 65536.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent arguments */
+  MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported set above */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+/* Layer dimensions.  The workload model uses {2048, 512, 256, 8, 64, 512}. */
+typedef struct moe_dims {
+  int32_t hidden;       /* H: token width */
+  int32_t inter;        /* I: intermediate width of a routed expert */
+  int32_t n_experts;    /* E: routed experts */
+  int32_t top_k;        /* k: experts kept per token */
+  int32_t group_size;   /* G: int4 quantisation group along the input dim (64) */
+  int32_t shared_inter; /* Is: intermediate width of the shared expert */
+} moe_dims;
+
+/* Affine int4 weights of n_exp experts (one matrix each), canonical layout:
+ *   codes  uint8 [n_exp][N][K/2]: element (n, k) in byte k/2, low nibble = even k
+ *   scales fp16  [n_exp][N][K/G], biases fp16 [n_exp][N][K/G]
+ * Weight value w = bf16_rne( fp32(code) * fp32(scale) + fp32(bias) ).
+ * gate_up matrices: N = 2*I (rows 0..I-1 gate, I..2I-1 up), K = H.
+ * down matrices:    N = H, K = I. */
+typedef struct moe_q4 {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* biases;
+} moe_q4;
+
+/* All weights of one layer. */
+typedef struct moe_layer {
+  moe_q4 gate_up;              /* routed experts, [E][2I][H] */
+  moe_q4 down;                 /* routed experts, [E][H][I] */
+  moe_q4 sh_gate_up;           /* shared expert, [1][2Is][H] */
+  moe_q4 sh_down;              /* shared expert, [1][H][Is] */
+  const float* router_w;       /* [E][H] fp32; read by the T == 1 path */
+  const float* router_bias;    /* [E] fp32 added to the logits, or NULL */
+  const float* shared_gate_w;  /* [H] fp32 */
+  const uint16_t* router_w3;   /* [3][E][H] bf16 from moe_prepack_router(); required when T > 1 */
+} moe_layer;
+
+/* Tile height (rows) that moe_forward uses for its block map. */
+int32_t moe_block_m(void);
+
+/* Entries a block map of tile height block_m may need: ceil(T*k/block_m) + E. */
+int32_t moe_max_tiles(int32_t T, int32_t top_k, int32_t n_experts, int32_t block_m);
+
+/* Split fp32 router weights [E][H] exactly into three bf16 planes
+ * router_w3[0] + router_w3[1] + router_w3[2] == router_w (each plane keeps the
+ * next 8 significant bits, truncating), so that bf16 matrix-core products of a
+ * bf16 activation with the planes are exact and the router stays fp32-accurate.
+ * A one-time weight preparation, like loading the checkpoint. */
+moe_status moe_prepack_router(const moe_dims* d, const float* router_w, uint16_t* router_w3, void* stream);
+
+/* Router logits (step: "a router scores 256 expert subnetworks", Lily page,
+ * section "The architecture that forces the issue: MoE plus Gated DeltaNet").
+ *   x [T][H] bf16 -> logits [T][E] fp32 = x . router_w^T (+ router_bias),
+ *                    shared_logit [T] fp32 = x . shared_gate_w  (NULL to skip).
+ * T == 1 reads router_w (fp32 vector ALU dot products); T > 1 needs
+ * layer->router_w3 (bf16 matrix cores, fp32 accumulation).  Only the router
+ * fields of `layer` are read. */
+moe_status moe_router_logits(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T,
+                             float* logits, float* shared_logit, void* stream);
+
+/* Top-k routing from logits ("... and picks 8", same section).
+ *   logits [T][E] fp32 -> ids [T][k] int32: the k largest logits in descending
+ *   order, equal logits (+0 == -0) ordered by the lower expert index;
+ *   weights [T][k] fp32: softmax over all E logits restricted to the kept
+ *   experts and renormalised to sum to 1, i.e. exp(l_j - l_0) / sum_j' exp(l_j' - l_0);
+ *   if shared_logit and gate are both non-NULL: gate[T] = 1 / (1 + exp(-shared_logit)).
+ * Deterministic.  Inputs must be finite. */
+moe_status moe_route(const moe_dims* d, const float* logits, const float* shared_logit, int32_t T, int32_t* ids,
+                     float* weights, float* gate, void* stream);
+
+/* Scratch bytes moe_group() needs for T tokens. */
+size_t moe_group_workspace_bytes(const moe_dims* d, int32_t T);
+
+/* GPU-resident grouping of the T*k routed slots by expert ("Routing histograms
+ * and block maps remain inside GPU command buffers", Inside Lily page, section
+ * "Performance Gains and Workload Patterns").  Flat slot f = t*k + j.
+ *   counts   [E]      slots per expert (sum = T*k)
+ *   offsets  [E+1]    exclusive prefix sum of counts, offsets[E] = T*k
+ *   perm     [T*k]    slots grouped by expert; within an expert ascending f (stable)
+ *   inv_perm [T*k]    inv_perm[perm[p]] = p
+ *   block_map[max_tiles][2] (expert, first row) for every tile of block_m rows,
+ *                     experts ascending; unused entries (-1, -1)
+ *   n_tiles  [1]      number of used entries (never leaves the device)
+ * max_tiles must be >= moe_max_tiles(T, k, E, block_m); 1 <= block_m <= 4096.
+ * ids values must lie in [0, E).  Bitwise deterministic. */
+moe_status moe_group(const moe_dims* d, const int32_t* ids, int32_t T, int32_t block_m, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* block_map, int32_t max_tiles,
+                     int32_t* n_tiles, void* workspace, size_t workspace_bytes, void* stream);
+
+typedef enum moe_epilogue {
+  /* h[p][n] = bf16( silu(gate) * up ), gate/up = a_row . W_gate_up[e]^T, a_row = x[perm[p] / k] */
+  MOE_EPI_SWIGLU_BF16 = 0,
+  /* y[perm[p] / k][m] += row_weight[perm[p]] * (h[p] . W_down[e]^T)[m]   (fp32 atomics) */
+  MOE_EPI_WEIGHTED_SCATTER_F32 = 1
+} moe_epilogue;
+
+/* Grouped GEMM over the tiles of a block map with int4 weights dequantised in
+ * registers (bf16 matrix cores, fp32 accumulation; "reconstructing 4-bit
+ * weights one tile at a time within grouped GEMM operations", Inside Lily page,
+ * section "Performance Gains and Workload Patterns").  Routed experts only.
+ *   SWIGLU:  a = x [T][H] bf16 (token rows, gathered through perm);
+ *            w = gate_up weights; out = h [T*k][I] bf16 in grouped order.
+ *   SCATTER: a = h [T*k][I] bf16 in grouped order; w = down weights;
+ *            row_weight [T*k] fp32 indexed by flat slot; out = y [T][H] fp32,
+ *            accumulated into (the caller zeroes it first).  Accumulation order
+ *            across experts is not fixed, so y is reproducible to fp32 rounding.
+ * perm/offsets/block_map/n_tiles as produced by moe_group() with the same
+ * block_m; 1 <= block_m <= moe_block_m(). */
+moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
+                               const int32_t* perm, const int32_t* offsets, const int32_t* block_map,
+                               const int32_t* n_tiles, int32_t max_tiles, const float* row_weight, int32_t T,
+                               int32_t block_m, void* out, void* stream);
+
+/* Scratch bytes moe_forward() needs for up to T_max tokens. */
+size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
+
+/* The whole layer for T tokens:
+ *   y[t] = bf16( sum_j w[t][j] * E_{ids[t][j]}(x[t]) + g[t] * E_shared(x[t]) ),
+ *   E(x) = ( silu(x.Wg^T) * (x.Wu^T) ) . Wd^T with the SwiGLU product rounded to bf16.
+ * T == 1 runs the decode path (vector-ALU GEMV, fp32 router_w); T > 1 runs
+ * router GEMM, top-k, grouping, the two grouped GEMMs and the combine on the
+ * matrix cores (needs router_w3).  No host synchronisation anywhere.
+ * Optional outputs (NULL to skip): logits_out [T][E], ids_out [T][k], w_out [T][k].
+ * workspace_bytes must be >= moe_workspace_bytes(d, T). */
+moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,
+                       float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Human-readable name of a status; message of the last failed check on this thread. */
+const char* moe_status_str(moe_status s);
+const char* moe_last_error_message(void);
+/* hipError_t of the last failed launch on this thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,239 @@
+"""Sparse Mixture-of-Experts layer for MI355X (gfx950): Python binding of libmoe.
+
+Thin ctypes marshalling over the C ABI declared in ``include/moe.h``: every
+function here has the name of the C entry point it calls, takes torch tensors
+for device memory and launches on ``torch.cuda.current_stream()``.  All work
+runs in the HIP kernels of ``libmoe.so``; if the library is not built, every
+call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # first: libmoe then binds to the HIP runtime torch already loaded
+
+__all__ = [
+    "Dims", "MoeError", "LayerWeights", "lib", "moe_block_m", "moe_max_tiles", "moe_prepack_router",
+    "moe_router_logits", "moe_route", "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4",
+    "moe_workspace_bytes", "moe_forward", "MOE_EPI_SWIGLU_BF16", "MOE_EPI_WEIGHTED_SCATTER_F32",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "moe_block_m", "moe_max_tiles", "moe_prepack_router", "moe_router_logits", "moe_route",
+    "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4", "moe_workspace_bytes", "moe_forward",
+    "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+@dataclass(frozen=True)
+class Dims:
+    hidden: int = 2048
+    inter: int = 512
+    n_experts: int = 256
+    top_k: int = 8
+    group_size: int = 64
+    shared_inter: int = 512
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("hidden", "inter", "n_experts", "top_k", "group_size", "shared_inter")]
+
+
+class _Q4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("gate_up", _Q4), ("down", _Q4), ("sh_gate_up", _Q4), ("sh_down", _Q4),
+                ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("shared_gate_w", ctypes.c_void_p), ("router_w3", ctypes.c_void_p)]
+
+
+_handle = None
+_P, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def lib():
+    """The loaded libmoe.so; raises if it has not been built."""
+    global _handle
+    if _handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        h = ctypes.CDLL(LIB_PATH)
+        PD, PL = ctypes.POINTER(_Dims), ctypes.POINTER(_Layer)
+        sig = {
+            "moe_block_m": ([], _I32),
+            "moe_max_tiles": ([_I32, _I32, _I32, _I32], _I32),
+            "moe_prepack_router": ([PD, _P, _P, _P], _I32),
+            "moe_router_logits": ([PD, PL, _P, _I32, _P, _P, _P], _I32),
+            "moe_route": ([PD, _P, _P, _I32, _P, _P, _P, _P], _I32),
+            "moe_group_workspace_bytes": ([PD, _I32], _SZ),
+            "moe_group": ([PD, _P, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], _I32),
+            "moe_grouped_gemm_q4": ([PD, ctypes.POINTER(_Q4), _I32, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P],
+                                    _I32),
+            "moe_workspace_bytes": ([PD, _I32], _SZ),
+            "moe_forward": ([PD, PL, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+            "moe_status_str": ([_I32], ctypes.c_char_p),
+            "moe_last_error_message": ([], ctypes.c_char_p),
+            "moe_last_hip_error": ([], _I32),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(h, name)
+            fn.argtypes = args
+            fn.restype = res
+        _handle = h
+    return _handle
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        L = lib()
+        raise MoeError(status, f"{L.moe_status_str(status).decode()}: {L.moe_last_error_message().decode()}")
+
+
+def _dims(d) -> _Dims:
+    return _Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _q4(m) -> _Q4:
+    c, s, b = m
+    return _Q4(_ptr(c), _ptr(s), _ptr(b))
+
+
+class LayerWeights:
+    """Device tensors of one layer and the C struct that points at them.
+
+    gate_up/down/sh_gate_up/sh_down: (codes uint8, scales int16, biases int16)
+    in the canonical layout of ``include/moe.h``.
+    """
+
+    def __init__(self, d, gate_up, down, sh_gate_up, sh_down, router_w, shared_gate_w, router_bias=None,
+                 router_w3=None):
+        self.d = d
+        self.gate_up, self.down, self.sh_gate_up, self.sh_down = gate_up, down, sh_gate_up, sh_down
+        self.router_w, self.shared_gate_w, self.router_bias = router_w, shared_gate_w, router_bias
+        self.router_w3 = router_w3 if router_w3 is not None else moe_prepack_router(d, router_w)
+        self.c = _Layer(_q4(gate_up), _q4(down), _q4(sh_gate_up), _q4(sh_down), _ptr(router_w), _ptr(router_bias),
+                        _ptr(shared_gate_w), _ptr(self.router_w3))
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def moe_block_m() -> int:
+    return int(lib().moe_block_m())
+
+
+def moe_max_tiles(T: int, top_k: int, n_experts: int, block_m: int) -> int:
+    return int(lib().moe_max_tiles(T, top_k, n_experts, block_m))
+
+
+def moe_prepack_router(d, router_w: torch.Tensor, router_w3: torch.Tensor | None = None) -> torch.Tensor:
+    if router_w3 is None:
+        router_w3 = _empty((3, d.n_experts, d.hidden), torch.int16, router_w)
+    _check(lib().moe_prepack_router(ctypes.byref(_dims(d)), _ptr(router_w), _ptr(router_w3), _stream()))
+    return router_w3
+
+
+def moe_router_logits(d, layer: LayerWeights, x: torch.Tensor, logits=None, shared_logit=None,
+                      want_shared: bool = True):
+    T = x.shape[0]
+    if logits is None:
+        logits = _empty((T, d.n_experts), torch.float32, x)
+    if shared_logit is None and want_shared:
+        shared_logit = _empty((T,), torch.float32, x)
+    _check(lib().moe_router_logits(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(logits),
+                                   _ptr(shared_logit), _stream()))
+    return logits, shared_logit
+
+
+def moe_route(d, logits: torch.Tensor, shared_logit=None, ids=None, weights=None, gate=None):
+    T = logits.shape[0]
+    if ids is None:
+        ids = _empty((T, d.top_k), torch.int32, logits)
+    if weights is None:
+        weights = _empty((T, d.top_k), torch.float32, logits)
+    if shared_logit is not None and gate is None:
+        gate = _empty((T,), torch.float32, logits)
+    _check(lib().moe_route(ctypes.byref(_dims(d)), _ptr(logits), _ptr(shared_logit), T, _ptr(ids), _ptr(weights),
+                           _ptr(gate), _stream()))
+    return ids, weights, gate
+
+
+def moe_group_workspace_bytes(d, T: int) -> int:
+    return int(lib().moe_group_workspace_bytes(ctypes.byref(_dims(d)), T))
+
+
+def moe_group(d, ids: torch.Tensor, block_m: int, max_tiles: int | None = None, out: dict | None = None,
+              workspace: torch.Tensor | None = None) -> dict:
+    T = ids.shape[0]
+    F = T * d.top_k
+    mt = moe_max_tiles(T, d.top_k, d.n_experts, block_m) if max_tiles is None else max_tiles
+    o = out if out is not None else {
+        "counts": _empty((d.n_experts,), torch.int32, ids), "offsets": _empty((d.n_experts + 1,), torch.int32, ids),
+        "perm": _empty((F,), torch.int32, ids), "inv_perm": _empty((F,), torch.int32, ids),
+        "block_map": _empty((mt, 2), torch.int32, ids), "n_tiles": _empty((1,), torch.int32, ids)}
+    if workspace is None:
+        workspace = _empty((max(1, moe_group_workspace_bytes(d, T)),), torch.uint8, ids)
+    _check(lib().moe_group(ctypes.byref(_dims(d)), _ptr(ids), T, block_m, _ptr(o["counts"]), _ptr(o["offsets"]),
+                           _ptr(o["perm"]), _ptr(o["inv_perm"]), _ptr(o["block_map"]), mt, _ptr(o["n_tiles"]),
+                           _ptr(workspace), workspace.numel(), _stream()))
+    o["max_tiles"] = mt
+    return o
+
+
+def moe_grouped_gemm_q4(d, w, epi: int, a: torch.Tensor, perm, offsets, block_map, n_tiles, max_tiles: int,
+                        row_weight, T: int, block_m: int, out: torch.Tensor):
+    q = _q4(w)
+    _check(lib().moe_grouped_gemm_q4(ctypes.byref(_dims(d)), ctypes.byref(q), epi, _ptr(a), _ptr(perm),
+                                     _ptr(offsets), _ptr(block_map), _ptr(n_tiles), max_tiles, _ptr(row_weight), T,
+                                     block_m, _ptr(out), _stream()))
+    return out
+
+
+def moe_workspace_bytes(d, T_max: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(_dims(d)), T_max))
+
+
+def moe_forward(d, layer: LayerWeights, x: torch.Tensor, y=None, logits_out=None, ids_out=None, w_out=None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    T = x.shape[0]
+    if y is None:
+        y = _empty((T, d.hidden), torch.bfloat16, x)
+    if workspace is None:
+        workspace = _empty((moe_workspace_bytes(d, T),), torch.uint8, x)
+    _check(lib().moe_forward(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y), _ptr(logits_out),
+                             _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(), _stream()))
+    return y

@@ -1,0 +1,287 @@
+// C ABI of libmoe: argument validation, workspace carving and the launch
+// sequence of every entry point.  Nothing here synchronises the host with the
+// device and nothing allocates device memory.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_msg[256] = "";
+thread_local int32_t g_hip_err = 0;
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status hip_check(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  g_hip_err = static_cast<int32_t>(e);
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+moe_status check_dims(const moe_dims* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "dims is NULL");
+  if (d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->group_size <= 0 ||
+      d->shared_inter <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "dims must be positive");
+  if (d->group_size != 64) return fail(MOE_ERR_UNSUPPORTED, "group_size must be 64");
+  if (d->hidden % 64) return fail(MOE_ERR_UNSUPPORTED, "hidden must be a multiple of 64");
+  if (d->inter % 32 || d->shared_inter % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "inter and shared_inter must be multiples of 32");
+  if (d->n_experts % 16 || d->n_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "n_experts must be 16..256, x16");
+  if (d->top_k > 16 || d->top_k > d->n_experts) return fail(MOE_ERR_UNSUPPORTED, "top_k must be <= 16 and <= n_experts");
+  return MOE_OK;
+}
+
+moe_status check_T(int32_t T) {
+  if (T < 1 || T > 65536) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [1, 65536]", T);
+  return MOE_OK;
+}
+
+moe_status check_q4(const moe_q4* q, const char* name) {
+  if (!q || !q->codes || !q->scales || !q->biases) return fail(MOE_ERR_INVALID_ARG, "%s: NULL weight pointer", name);
+  return MOE_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace regions of moe_forward.
+struct Ws {
+  size_t logits, s, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh, y, hdec;
+  size_t total;
+};
+
+Ws layout(const moe_dims& d, int32_t T) {
+  const size_t E = d.n_experts, k = d.top_k, H = d.hidden, I = d.inter, Is = d.shared_inter;
+  const size_t F = static_cast<size_t>(T) * k;
+  const size_t ntile = static_cast<size_t>(div_up(T, kTopkTile));
+  const size_t mt = static_cast<size_t>(moe_max_tiles(T, d.top_k, d.n_experts, kBM));
+  const size_t ldh = static_cast<size_t>(div_up(std::max(I, Is), 8) * 8);
+  Ws w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  w.logits = take(T * E * 4);
+  w.s = take(T * 4);
+  w.ids = take(F * 4);
+  w.wts = take(F * 4);
+  w.gate = take(T * 4);
+  w.tilehist = take(ntile * E * 4);
+  w.tilebase = take(ntile * E * 4);
+  w.counts = take(E * 4);
+  w.offsets = take((E + 1) * 4);
+  w.perm = take(F * 4);
+  w.inv = take(F * 4);
+  w.bmap = take(mt * 2 * 4);
+  w.ntiles = take(4);
+  w.h = take(F * I * 2);
+  w.hsh = take(static_cast<size_t>(T) * Is * 2);
+  w.y = take(static_cast<size_t>(T) * H * 4);
+  w.hdec = take((k + 1) * ldh * 2);
+  w.total = o;
+  return w;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_block_m(void) { return kBM; }
+
+int32_t moe_max_tiles(int32_t T, int32_t top_k, int32_t n_experts, int32_t block_m) {
+  if (T < 0 || top_k < 1 || n_experts < 1 || block_m < 1) return 0;
+  return static_cast<int32_t>(div_up(static_cast<int64_t>(T) * top_k, block_m) + n_experts);
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error_message(void) { return g_msg; }
+int32_t moe_last_hip_error(void) { return g_hip_err; }
+
+moe_status moe_prepack_router(const moe_dims* d, const float* router_w, uint16_t* router_w3, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if (!router_w || !router_w3) return fail(MOE_ERR_INVALID_ARG, "NULL router weights");
+  return hip_check(launch_prepack_router(router_w, router_w3, d->n_experts, d->hidden,
+                                         static_cast<hipStream_t>(stream)),
+                   "moe_prepack_router");
+}
+
+moe_status moe_router_logits(const moe_dims* d, const moe_layer* L, const uint16_t* x, int32_t T, float* logits,
+                             float* shared_logit, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  if (!L || !x || !logits) return fail(MOE_ERR_INVALID_ARG, "NULL layer, x or logits");
+  if (shared_logit && !L->shared_gate_w) return fail(MOE_ERR_INVALID_ARG, "shared_logit needs shared_gate_w");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 1) {
+    if (!L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+    return hip_check(launch_router_gemv(x, L->router_w, L->router_bias, L->shared_gate_w, 1, d->hidden,
+                                        d->n_experts, logits, shared_logit, s),
+                     "router gemv");
+  }
+  if (!L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
+  return hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, shared_logit ? L->shared_gate_w : nullptr, T,
+                                      d->hidden, d->n_experts, logits, shared_logit, nullptr, s),
+                   "router gemm");
+}
+
+moe_status moe_route(const moe_dims* d, const float* logits, const float* shared_logit, int32_t T, int32_t* ids,
+                     float* weights, float* gate, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  if (!logits || !ids || !weights) return fail(MOE_ERR_INVALID_ARG, "NULL logits, ids or weights");
+  if ((gate != nullptr) != (shared_logit != nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "shared_logit and gate must both be given or both be NULL");
+  return hip_check(launch_topk(logits, shared_logit, T, d->n_experts, d->top_k, ids, weights, gate, nullptr,
+                               static_cast<hipStream_t>(stream)),
+                   "top-k");
+}
+
+size_t moe_group_workspace_bytes(const moe_dims* d, int32_t T) {
+  if (check_dims(d) || check_T(T)) return 0;
+  const size_t ntile = static_cast<size_t>(div_up(T, kTopkTile));
+  return 2 * align256(ntile * d->n_experts * 4);
+}
+
+moe_status moe_group(const moe_dims* d, const int32_t* ids, int32_t T, int32_t block_m, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* block_map, int32_t max_tiles,
+                     int32_t* n_tiles, void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  if (!ids || !counts || !offsets || !perm || !inv_perm || !block_map || !n_tiles)
+    return fail(MOE_ERR_INVALID_ARG, "NULL output pointer");
+  if (block_m < 1 || block_m > 4096) return fail(MOE_ERR_INVALID_ARG, "block_m=%d outside [1, 4096]", block_m);
+  if (max_tiles < moe_max_tiles(T, d->top_k, d->n_experts, block_m))
+    return fail(MOE_ERR_INVALID_ARG, "max_tiles=%d < %d", max_tiles, moe_max_tiles(T, d->top_k, d->n_experts, block_m));
+  const size_t need = moe_group_workspace_bytes(d, T);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t ntile = static_cast<size_t>(div_up(T, kTopkTile));
+  int32_t* tilehist = at<int32_t>(workspace, 0);
+  int32_t* tilebase = at<int32_t>(workspace, align256(ntile * d->n_experts * 4));
+  if ((st = hip_check(launch_tile_hist(ids, T, d->top_k, d->n_experts, tilehist, s), "tile histogram"))) return st;
+  return hip_check(launch_group(ids, tilehist, tilebase, T, d->top_k, d->n_experts, block_m, counts, offsets, perm,
+                                inv_perm, block_map, max_tiles, n_tiles, s),
+                   "grouping");
+}
+
+moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
+                               const int32_t* perm, const int32_t* offsets, const int32_t* block_map,
+                               const int32_t* n_tiles, int32_t max_tiles, const float* row_weight, int32_t T,
+                               int32_t block_m, void* out, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  if ((st = check_q4(w, "w"))) return st;
+  if (!a || !perm || !offsets || !block_map || !n_tiles || !out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (block_m < 1 || block_m > kBM) return fail(MOE_ERR_INVALID_ARG, "block_m=%d outside [1, %d]", block_m, kBM);
+  if (max_tiles < 1) return fail(MOE_ERR_INVALID_ARG, "max_tiles must be positive");
+  GemmTiles tl{perm, offsets, block_map, n_tiles, max_tiles, block_m, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (epi == MOE_EPI_SWIGLU_BF16)
+    return hip_check(launch_gemm_swiglu(*d, *w, nullptr, a, tl, T, static_cast<uint16_t*>(out), nullptr, s),
+                     "grouped gemm (swiglu)");
+  if (epi == MOE_EPI_WEIGHTED_SCATTER_F32) {
+    if (!row_weight) return fail(MOE_ERR_INVALID_ARG, "row_weight is NULL");
+    return hip_check(
+        launch_gemm_scatter(*d, *w, nullptr, a, nullptr, tl, row_weight, nullptr, T, static_cast<float*>(out), s),
+        "grouped gemm (scatter)");
+  }
+  return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", static_cast<int>(epi));
+}
+
+size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max) {
+  if (check_dims(d) || check_T(T_max)) return 0;
+  return layout(*d, T_max).total;
+}
+
+moe_status moe_forward(const moe_dims* d, const moe_layer* L, const uint16_t* x, int32_t T, uint16_t* y,
+                       float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  if (!L || !x || !y) return fail(MOE_ERR_INVALID_ARG, "NULL layer, x or y");
+  if ((st = check_q4(&L->gate_up, "gate_up")) || (st = check_q4(&L->down, "down")) ||
+      (st = check_q4(&L->sh_gate_up, "sh_gate_up")) || (st = check_q4(&L->sh_down, "sh_down")))
+    return st;
+  if (!L->shared_gate_w) return fail(MOE_ERR_INVALID_ARG, "shared_gate_w is NULL");
+  const Ws w = layout(*d, T);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, w.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = logits_out ? logits_out : at<float>(workspace, w.logits);
+  int32_t* ids = ids_out ? ids_out : at<int32_t>(workspace, w.ids);
+  float* wts = w_out ? w_out : at<float>(workspace, w.wts);
+  float* s_logit = at<float>(workspace, w.s);
+  float* gate = at<float>(workspace, w.gate);
+
+  if (T == 1) {
+    if (!L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+    return hip_check(launch_decode(*d, *L, x, y, logits, s_logit, ids, wts, gate, at<uint16_t>(workspace, w.hdec), s),
+                     "decode");
+  }
+  if (!L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
+  float* yacc = at<float>(workspace, w.y);
+  int32_t* tilehist = at<int32_t>(workspace, w.tilehist);
+  int32_t* counts = at<int32_t>(workspace, w.counts);
+  int32_t* offsets = at<int32_t>(workspace, w.offsets);
+  int32_t* perm = at<int32_t>(workspace, w.perm);
+  int32_t* bmap = at<int32_t>(workspace, w.bmap);
+  int32_t* ntiles = at<int32_t>(workspace, w.ntiles);
+  uint16_t* h = at<uint16_t>(workspace, w.h);
+  uint16_t* hsh = at<uint16_t>(workspace, w.hsh);
+  const int E = d->n_experts, k = d->top_k;
+  const int mt = moe_max_tiles(T, k, E, kBM);
+
+  if ((st = hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, L->shared_gate_w, T, d->hidden, E, logits,
+                                         s_logit, yacc, s),
+                      "router gemm")))
+    return st;
+  if ((st = hip_check(launch_topk(logits, s_logit, T, E, k, ids, wts, gate, tilehist, s), "top-k"))) return st;
+  if ((st = hip_check(launch_group(ids, tilehist, at<int32_t>(workspace, w.tilebase), T, k, E, kBM, counts, offsets,
+                                   perm, at<int32_t>(workspace, w.inv), bmap, mt, ntiles, s),
+                      "grouping")))
+    return st;
+  GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM))};
+  if ((st = hip_check(launch_gemm_swiglu(*d, L->gate_up, &L->sh_gate_up, x, tl, T, h, hsh, s), "gate/up gemm")))
+    return st;
+  if ((st = hip_check(launch_gemm_scatter(*d, L->down, &L->sh_down, h, hsh, tl, wts, gate, T, yacc, s), "down gemm")))
+    return st;
+  return hip_check(launch_finalize(yacc, y, static_cast<int64_t>(T) * d->hidden, s), "finalize");
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// GPU-resident grouping of routed slots by expert: histogram, prefix-sum
+// offsets, stable permutation and tile block map, with no host round trip
+// ("Routing histograms and block maps remain inside GPU command buffers,
+// preventing costly CPU-to-GPU synchronization": Inside Lily page, section
+// "Performance Gains and Workload Patterns").
+//
+// Three steps, all on the device:
+//   1. per routing tile (64 tokens): expert histogram          (k_tile_hist, or fused into k_topk)
+//   2. per expert: exclusive scan of its count over the tiles  (k_group_scan, one block per expert)
+//   3. per tile: stable in-tile ranks from wavefront ballots,
+//      positions = offsets[e] + tile base + rank               (k_group_scatter)
+// Integer counting only, so every output is bitwise deterministic.
+#include "internal.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                   int32_t* __restrict__ tilehist) {
+  __shared__ int hist[256];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTopkTile * k;
+  const int64_t f1 = min(static_cast<int64_t>(T) * k, f0 + static_cast<int64_t>(kTopkTile) * k);
+  for (int64_t f = f0 + threadIdx.x; f < f1; f += 256) atomicAdd(&hist[ids[f]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) tilehist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
+}
+
+hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, hipStream_t s) {
+  hipLaunchKernelGGL(k_tile_hist, dim3(static_cast<unsigned>(div_up(T, kTopkTile))), dim3(256), 0, s, ids, T, k, E,
+                     tilehist);
+  return hipGetLastError();
+}
+
+// Exclusive scan of one value per thread over a 256-thread block; returns the
+// exclusive prefix and writes the block total to *total.
+__device__ inline int block_excl_scan256(int v, int* sm, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sm[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += sm[w];
+  const int tot = sm[0] + sm[1] + sm[2] + sm[3];
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
+}
+
+// Block e: exclusive prefix of tilehist[.][e] over the tiles -> tilebase, total -> counts[e].
+__global__ __launch_bounds__(256) void k_group_scan(const int32_t* __restrict__ tilehist,
+                                                    int32_t* __restrict__ tilebase, int ntile, int E,
+                                                    int32_t* __restrict__ counts) {
+  __shared__ int sm[4];
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int base = 0; base < ntile; base += 256) {
+    const int i = base + threadIdx.x;
+    const int v = (i < ntile) ? tilehist[static_cast<int64_t>(i) * E + e] : 0;
+    int tot;
+    const int ex = block_excl_scan256(v, sm, &tot);
+    if (i < ntile) tilebase[static_cast<int64_t>(i) * E + e] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// Block b = routing tile b.  All threads: offsets = exclusive scan of counts,
+// running base[e] = offsets[e] + tilebase[b][e].  Wave 0 then walks the tile's
+// flat slots in order, 64 at a time: lanes with equal expert id find each
+// other through 8 ballots (one per id bit), the rank of a lane is the number
+// of matching lower lanes, and the group's count advances base[e].  Block 0
+// also writes offsets, the block map and n_tiles.
+__global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids,
+                                                       const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ tilebase, int T, int k, int E,
+                                                       int block_m, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                       int32_t* __restrict__ block_map, int max_tiles,
+                                                       int32_t* __restrict__ n_tiles) {
+  __shared__ int base[256];
+  __shared__ int sm[4];
+  const int tid = threadIdx.x;
+  const int c = (tid < E) ? counts[tid] : 0;
+  int total;
+  const int off = block_excl_scan256(c, sm, &total);
+  if (tid < E) base[tid] = off + tilebase[static_cast<int64_t>(blockIdx.x) * E + tid];
+
+  if (blockIdx.x == 0) {
+    const int nt = (c + block_m - 1) / block_m;
+    int nt_total;
+    const int toff = block_excl_scan256(nt, sm, &nt_total);
+    if (tid < E) {
+      offsets[tid] = off;
+      for (int m = 0; m < nt; ++m) {
+        block_map[2 * (toff + m)] = tid;
+        block_map[2 * (toff + m) + 1] = off + m * block_m;
+      }
+    }
+    if (tid == 0) {
+      offsets[E] = total;
+      *n_tiles = nt_total;
+    }
+    for (int i = nt_total + tid; i < max_tiles; i += 256) {
+      block_map[2 * i] = -1;
+      block_map[2 * i + 1] = -1;
+    }
+  }
+  __syncthreads();
+
+  if (tid < 64) {
+    const int lane = tid;
+    const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+    const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTopkTile * k;
+    const int64_t f1 = min(static_cast<int64_t>(T) * k, f0 + static_cast<int64_t>(kTopkTile) * k);
+    for (int64_t fb = f0; fb < f1; fb += 64) {
+      const int64_t f = fb + lane;
+      const bool valid = f < f1;
+      const int e = valid ? ids[f] : 0;
+      uint64_t match = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint64_t bal = __ballot((e >> b) & 1);
+        match &= ((e >> b) & 1) ? bal : ~bal;
+      }
+      const int rank = __popcll(match & lt);
+      const int pos = base[e] + rank;  // every lane reads before any lane updates
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        perm[pos] = static_cast<int32_t>(f);
+        inv_perm[f] = pos;
+        if (rank == 0) base[e] = pos + __popcll(match);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
+                        int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        int32_t* block_map, int max_tiles, int32_t* n_tiles, hipStream_t s) {
+  const int ntile = static_cast<int>(div_up(T, kTopkTile));
+  hipLaunchKernelGGL(k_group_scan, dim3(E), dim3(256), 0, s, tilehist, tilebase, ntile, E, counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_group_scatter, dim3(ntile), dim3(256), 0, s, ids, counts, tilebase, T, k, E, block_m, offsets,
+                     perm, inv_perm, block_map, max_tiles, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

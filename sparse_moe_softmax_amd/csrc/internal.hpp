@@ -1,0 +1,189 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+// Written for gfx950 (CDNA4): 64-lane wavefronts, bf16 MFMA 16x16x32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ vector types
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Tile height of the grouped GEMMs (rows of one block-map entry) and the
+// weight columns one wave owns.
+constexpr int kBM = 128;
+constexpr int kMSub = kBM / 16;     // 16-row MFMA sub-tiles per tile
+constexpr int kTopkTile = 64;       // tokens per routing tile (histogram granularity)
+
+// ------------------------------------------------------------------ scalar helpers
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  // one v_cvt_pk_bf16_f32: round-to-nearest-even of both values
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ inline uint16_t f32_to_bf16_bits(float v) { return static_cast<uint16_t>(pack_bf16x2(v, 0.f)); }
+
+// Dequantise the 8 int4 codes of one dword (element i in nibble i, low nibble
+// first) to 8 bf16 values w = bf16_rne(c*s + b), returned as 4 packed dwords
+// (element 2j in the low half of dword j).
+//
+// Each nibble is isolated into a 16-bit half, where as an fp16 bit pattern it
+// is the subnormal c*2^-24 (nibbles 0, 2) or c*2^-20 (nibbles 1, 3 of a byte
+// pair, left in place x16); v_fma_mix_f32 widens the half exactly and computes
+// c*(s*2^24)*2^-24 + b with a single rounding of an exact value, i.e. the fp32
+// value c*s + b (c*s is exact in fp32: a 4-bit by 11-bit product).
+__device__ inline uint4 dequant8(uint32_t q, float s24, float s20, float bias) {
+  const uint32_t t0 = q & 0x000F000Fu;          // elements 0 | 4
+  const uint32_t t1 = q & 0x00F000F0u;          // elements 1 | 5   (x16)
+  const uint32_t qs = q >> 8;
+  const uint32_t t2 = qs & 0x000F000Fu;         // elements 2 | 6
+  const uint32_t t3 = qs & 0x00F000F0u;         // elements 3 | 7   (x16)
+  const f16x2 h0 = __builtin_bit_cast(f16x2, t0);
+  const f16x2 h1 = __builtin_bit_cast(f16x2, t1);
+  const f16x2 h2 = __builtin_bit_cast(f16x2, t2);
+  const f16x2 h3 = __builtin_bit_cast(f16x2, t3);
+  const float v0 = __builtin_fmaf(static_cast<float>(h0.x), s24, bias);
+  const float v4 = __builtin_fmaf(static_cast<float>(h0.y), s24, bias);
+  const float v1 = __builtin_fmaf(static_cast<float>(h1.x), s20, bias);
+  const float v5 = __builtin_fmaf(static_cast<float>(h1.y), s20, bias);
+  const float v2 = __builtin_fmaf(static_cast<float>(h2.x), s24, bias);
+  const float v6 = __builtin_fmaf(static_cast<float>(h2.y), s24, bias);
+  const float v3 = __builtin_fmaf(static_cast<float>(h3.x), s20, bias);
+  const float v7 = __builtin_fmaf(static_cast<float>(h3.y), s20, bias);
+  uint4 r;
+  r.x = pack_bf16x2(v0, v1);
+  r.y = pack_bf16x2(v2, v3);
+  r.z = pack_bf16x2(v4, v5);
+  r.w = pack_bf16x2(v6, v7);
+  return r;
+}
+
+// Per-group constants for dequant8 from fp16 scale / bias bit patterns.
+struct DqConst {
+  float s24, s20, bias;
+};
+__device__ inline DqConst dq_const(uint16_t scale_bits, uint16_t bias_bits) {
+  const float s = static_cast<float>(__builtin_bit_cast(_Float16, scale_bits));
+  DqConst c;
+  c.s24 = s * 16777216.0f;  // exact: power-of-two scaling
+  c.s20 = s * 1048576.0f;
+  c.bias = static_cast<float>(__builtin_bit_cast(_Float16, bias_bits));
+  return c;
+}
+
+__device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ top-k (device helpers)
+
+// Top-k of one token's E logits by a group of 16 lanes.  Lane j holds the
+// logits of experts j, j+16, j+32, ...; each of the k rounds takes every
+// lane's best unselected logit and reduces over the group with the order
+// "larger logit first, then lower expert index".  Results are identical in
+// all 16 lanes: top_e[r], top_v[r] for r < k.
+__device__ inline void topk16(const float* __restrict__ row, int E, int k, int j, int (&top_e)[16],
+                              float (&top_v)[16]) {
+  float v[16];
+  const int nper = E >> 4;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = (i < nper) ? row[i * 16 + j] : 0.f;
+  uint32_t sel = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < k) {
+      float bv = 0.f;
+      int be = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // ascending i = ascending expert id inside a lane: strict '>' keeps the lower id on ties
+        if (i < nper && !((sel >> i) & 1u) && (be == 0x7FFFFFFF || v[i] > bv)) {
+          bv = v[i];
+          be = i * 16 + j;
+        }
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 16);
+        const int oe = __shfl_xor(be, off, 16);
+        const bool take = (oe != 0x7FFFFFFF) && (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
+        bv = take ? ov : bv;
+        be = take ? oe : be;
+      }
+      if ((be & 15) == j) sel |= 1u << (be >> 4);
+      top_e[r] = be;
+      top_v[r] = bv;
+    }
+  }
+}
+
+// Renormalised weights of the k kept experts: exp(l_r - l_0) / sum_r' exp(l_r' - l_0),
+// summed in slot order.
+__device__ inline void topk_weights(int k, const float (&top_v)[16], float (&w)[16]) {
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < k) {
+      w[r] = expf(top_v[r] - top_v[0]);
+      sum += w[r];
+    }
+  }
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (r < k) w[r] = w[r] * inv;
+}
+
+__device__ inline float sigmoidf_(float s) { return 1.0f / (1.0f + expf(-s)); }
+
+// ------------------------------------------------------------------ launch helpers (host)
+
+struct GemmTiles {
+  const int32_t* perm;       // grouped position -> flat slot (routed tiles)
+  const int32_t* offsets;    // [E+1]
+  const int32_t* block_map;  // [max_tiles][2]
+  const int32_t* n_tiles;    // device scalar
+  int32_t max_tiles;         // routed tile bound (grid sizing)
+  int32_t block_m;           // rows per routed tile (<= kBM)
+  int32_t n_shared_chunks;   // shared-expert tiles of kBM rows put first (0 = none)
+};
+
+hipError_t launch_prepack_router(const float* w, uint16_t* w3, int E, int H, hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w3, const float* bias, const float* wsg, int T,
+                              int H, int E, float* logits, float* s_logit, float* y_zero, hipStream_t s);
+hipError_t launch_router_gemv(const uint16_t* x, const float* w, const float* bias, const float* wsg, int T, int H,
+                              int E, float* logits, float* s_logit, hipStream_t s);
+hipError_t launch_topk(const float* logits, const float* s_logit, int T, int E, int k, int32_t* ids, float* wts,
+                       float* gate, int32_t* tilehist, hipStream_t s);
+hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, hipStream_t s);
+hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
+                        int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        int32_t* block_map, int max_tiles, int32_t* n_tiles, hipStream_t s);
+hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* x,
+                              const GemmTiles& tl, int T, uint16_t* h, uint16_t* h_sh, hipStream_t s);
+hipError_t launch_gemm_scatter(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
+                               const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate,
+                               int T, float* y, hipStream_t s);
+hipError_t launch_finalize(const float* y, uint16_t* out, int64_t n, hipStream_t s);
+hipError_t launch_decode(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y, float* logits,
+                         float* s_logit, int32_t* ids, float* wts, float* gate, uint16_t* h_ws, hipStream_t s);
+
+__host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace moe

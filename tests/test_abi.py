@@ -1,0 +1,108 @@
+"""The C-ABI library: it loads, exports every symbol include/moe.h declares,
+and rejects bad arguments on the host before any launch (CPU only: no
+compute call is made)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import sparse_moe_softmax_amd
+    return sparse_moe_softmax_amd
+
+
+def test_every_declared_symbol_is_exported(m):
+    names = _declared()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(m.EXPORTED_SYMBOLS) == names
+
+
+def test_small_helpers(m):
+    assert m.moe_block_m() == 128
+    assert m.moe_max_tiles(4096, 8, 256, 128) == 256 + 256
+    assert m.moe_max_tiles(1, 8, 256, 128) == 1 + 256
+    L = m.lib()
+    for s, name in [(0, "MOE_OK"), (-1, "MOE_ERR_INVALID_ARG"), (-2, "MOE_ERR_UNSUPPORTED"),
+                    (-3, "MOE_ERR_WORKSPACE"), (-4, "MOE_ERR_HIP")]:
+        assert L.moe_status_str(s).decode() == name
+
+
+def _d(m, **kw):
+    return ctypes.byref(m._dims(m.Dims(**kw)))
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"group_size": 32}, -2), ({"hidden": 96}, -2), ({"inter": 48}, -2), ({"n_experts": 512}, -2),
+    ({"n_experts": 24}, -2), ({"top_k": 17}, -2), ({"top_k": 0}, -1), ({"hidden": -64}, -1)])
+def test_bad_dims_rejected(m, kw, status):
+    L = m.lib()
+    assert L.moe_route(_d(m, **kw), FAKE, None, 4, FAKE, FAKE, None, None) == status
+    assert L.moe_forward(_d(m, **kw), None, FAKE, 4, FAKE, None, None, None, FAKE, 1 << 30, None) == status
+    assert L.moe_workspace_bytes(_d(m, **kw), 4) == 0
+
+
+def test_bad_arguments_rejected(m):
+    L = m.lib()
+    d = _d(m)
+    assert L.moe_route(d, FAKE, None, 0, FAKE, FAKE, None, None) == -1          # T = 0
+    assert L.moe_route(d, FAKE, None, 70000, FAKE, FAKE, None, None) == -1      # T too large
+    assert L.moe_route(d, None, None, 4, FAKE, FAKE, None, None) == -1          # NULL logits
+    assert L.moe_route(d, FAKE, FAKE, 4, FAKE, FAKE, None, None) == -1          # gate without output
+    assert L.moe_forward(d, None, FAKE, 4, FAKE, None, None, None, FAKE, 1 << 30, None) == -1   # NULL layer
+    # group: block map too small, bad block_m, workspace too small
+    need = L.moe_group_workspace_bytes(d, 100)
+    assert need > 0
+    mt = L.moe_max_tiles(100, 8, 256, 64)
+    args = lambda bm, mtiles, ws: (d, FAKE, 100, bm, FAKE, FAKE, FAKE, FAKE, FAKE, mtiles, FAKE, FAKE, ws, None)
+    assert L.moe_group(*args(64, mt - 1, need)) == -1
+    assert L.moe_group(*args(0, mt, need)) == -1
+    assert L.moe_group(*args(64, mt, need - 1)) == -3
+    # grouped gemm: block_m above the kernel tile, scatter without weights, unknown epilogue
+    q = m._Q4(FAKE, FAKE, FAKE)
+    g = lambda epi, bm, rw: L.moe_grouped_gemm_q4(d, ctypes.byref(q), epi, FAKE, FAKE, FAKE, FAKE, FAKE, 10, rw,
+                                                  100, bm, FAKE, None)
+    assert g(0, 129, None) == -1
+    assert g(1, 64, None) == -1
+    assert g(7, 64, FAKE) == -1
+    assert "epilogue" in L.moe_last_error_message().decode()
+
+
+def test_forward_workspace_checked(m):
+    L = m.lib()
+    d = _d(m)
+    need = L.moe_workspace_bytes(d, 4096)
+    assert need > L.moe_workspace_bytes(d, 64) > 0
+    q = m._Q4(FAKE, FAKE, FAKE)
+    layer = m._Layer(q, q, q, q, FAKE, None, FAKE, FAKE)
+    assert L.moe_forward(d, ctypes.byref(layer), FAKE, 4096, FAKE, None, None, None, FAKE, need - 1, None) == -3
+    assert L.moe_forward(d, ctypes.byref(layer), FAKE, 4096, FAKE, None, None, None, None, need, None) == -3
+    nolayer = m._Layer(q, q, q, q, FAKE, None, None, FAKE)
+    assert L.moe_forward(d, ctypes.byref(nolayer), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
+    nor3 = m._Layer(q, q, q, q, FAKE, None, FAKE, None)
+    assert L.moe_forward(d, ctypes.byref(nor3), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
+
+
+def test_binding_refuses_host_tensors(m):
+    import torch
+    with pytest.raises(ValueError):
+        m.moe_route(m.Dims(), torch.zeros(4, 256))

@@ -1,0 +1,285 @@
+"""GPU parity of every step of the MoE layer against the CPU oracle.
+
+Each test calls the HIP library through its C ABI (via the ctypes binding) on
+seeded synthetic inputs and compares with the oracle element by element:
+bit-exact for routing ids, counts, offsets, permutations, block maps and tile
+counts; within the stated tolerances for floating point.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.Dims(hidden=128, inter=64, n_experts=16, top_k=4, group_size=64, shared_inter=64)
+MODEL = synth.MODEL_DIMS
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ generator / prepack
+
+def test_generator_cpu_gpu_identical():
+    say("generator cpu vs gpu")
+    for m, (N, K) in {"gate_up": (1024, 2048), "down": (2048, 512)}.items():
+        c1, s1, b1 = synth.q4_matrix(3, N, K, 64, seed=7, layer=5, matrix=m, device="cpu")
+        c2, s2, b2 = synth.q4_matrix(3, N, K, 64, seed=7, layer=5, matrix=m, device="cuda")
+        assert torch.equal(c1, c2.cpu()) and torch.equal(s1, s2.cpu()) and torch.equal(b1, b2.cpu())
+
+
+def test_prepack_router_is_exact_split():
+    say("prepack router")
+    m = gu.moe()
+    W = synth.router_weights(256, 2048, seed=3)
+    W[0, :4] = torch.tensor([0.0, -0.0, 1e-20, -3.5e-25])
+    w3 = m.moe_prepack_router(gu.to_dims(MODEL), W.cuda())
+    torch.cuda.synchronize()
+    planes = w3.cpu().view(torch.bfloat16).to(torch.float64)
+    assert torch.equal(planes.sum(0), W.to(torch.float64))
+
+
+# ------------------------------------------------------------------ router logits
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 300])
+def test_router_logits(T):
+    say("router logits T", T)
+    m = gu.moe()
+    lay = synth.make_layer(MODEL, 31, zipf_bias=(T == 65))
+    dl = gu.device_layer(lay, MODEL)
+    x = synth.activations(T, MODEL.hidden, 31)
+    logits, s = m.moe_router_logits(gu.to_dims(MODEL), dl, x.cuda())
+    torch.cuda.synchronize()
+    ow = gu.oracle_layer(lay)
+    ol, os_ = oracle.router(synth.bf16_bits_numpy(x), ow.router_w, ow.router_bias, ow.shared_gate_w)
+    assert np.abs(logits.cpu().numpy() - ol).max() <= gu.LOGIT_ATOL
+    assert np.abs(s.cpu().numpy() - os_).max() <= gu.LOGIT_ATOL
+
+
+# ------------------------------------------------------------------ top-k
+
+def _tie_logits(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    for t in range(0, T, 2):
+        o = np.argsort(-l[t], kind="stable")
+        l[t, o[k]] = l[t, o[k - 1]]          # tie across the cut
+        l[t, o[2]] = l[t, o[1]]              # tie among the kept
+    if T > 3:
+        l[1, :] = 0.0
+        l[1, ::3] = -0.0                     # +0 / -0 ties
+        l[3, :] = np.float32(2.5)            # all equal
+    return l
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (100, 256, 8), (513, 256, 8), (40, 16, 4), (33, 64, 16)])
+def test_route_bit_exact(T, E, k):
+    say("route T E k", T, E, k)
+    m = gu.moe()
+    d = synth.Dims(hidden=2048, inter=512, n_experts=E, top_k=k, group_size=64, shared_inter=512)
+    l = _tie_logits(T, E, k, T + E)
+    s = np.random.default_rng(1).standard_normal(T).astype(np.float32) * 3
+    ids, w, g = m.moe_route(gu.to_dims(d), torch.from_numpy(l).cuda(), torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    oids, ow = oracle.topk(l, k)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.abs(w.cpu().numpy() - ow).max() <= gu.WEIGHT_ATOL
+    assert np.abs(g.cpu().numpy() - oracle.sigmoid(s)).max() <= gu.WEIGHT_ATOL
+
+
+# ------------------------------------------------------------------ grouping
+
+def _ids(T, E, k, mode, seed):
+    rng = np.random.default_rng(seed)
+    if mode == "one_hot":
+        ids = np.tile(np.arange(k, dtype=np.int32)[::-1] + 5, (T, 1))
+        return ids
+    p = None
+    if mode == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        p = p[rng.permutation(E)]
+        p /= p.sum()
+    return np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,bm,mode", [
+    (1, 256, 8, 128, "uniform"), (64, 256, 8, 128, "uniform"), (65, 256, 8, 16, "uniform"),
+    (512, 256, 8, 128, "uniform"), (4096, 256, 8, 128, "uniform"), (16384, 256, 8, 128, "zipf"),
+    (200, 16, 4, 7, "one_hot"), (1000, 256, 8, 1, "zipf"), (129, 64, 16, 64, "uniform")])
+def test_group_bit_exact(T, E, k, bm, mode):
+    say("group T E k bm mode", T, E, k, bm, mode)
+    m = gu.moe()
+    d = synth.Dims(hidden=2048, inter=512, n_experts=E, top_k=k, group_size=64, shared_inter=512)
+    ids = _ids(T, E, k, mode, T * 3 + bm)
+    out = m.moe_group(gu.to_dims(d), torch.from_numpy(ids).cuda(), bm)
+    torch.cuda.synchronize()
+    ref = oracle.group(ids, E, bm, n_max_tiles=out["max_tiles"])
+    assert np.array_equal(out["counts"].cpu().numpy(), ref.counts)
+    assert np.array_equal(out["offsets"].cpu().numpy(), ref.offsets)
+    assert np.array_equal(out["perm"].cpu().numpy(), ref.perm)
+    assert np.array_equal(out["inv_perm"].cpu().numpy(), ref.inv_perm)
+    assert np.array_equal(out["block_map"].cpu().numpy(), ref.block_map)
+    assert int(out["n_tiles"].item()) == ref.n_tiles
+
+
+def test_group_is_deterministic():
+    say("group determinism")
+    m = gu.moe()
+    ids = torch.from_numpy(_ids(4096, 256, 8, "zipf", 5)).cuda()
+    a = m.moe_group(gu.to_dims(MODEL), ids, 128)
+    b = m.moe_group(gu.to_dims(MODEL), ids, 128)
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "perm", "inv_perm", "block_map", "n_tiles"):
+        assert torch.equal(a[key], b[key])
+
+
+# ------------------------------------------------------------------ grouped GEMMs
+
+def _grouped_case(d, T, seed, mode="uniform", block_m=128):
+    lay = synth.make_layer(d, seed)
+    x = synth.activations(T, d.hidden, seed)
+    ids = _ids(T, d.n_experts, d.top_k, mode, seed)
+    gr = oracle.group(ids, d.n_experts, block_m)
+    return lay, x, ids, gr
+
+
+def _h_compare(h_gpu_bits, h_ref_bits):
+    g = oracle.bf16_to_double(h_gpu_bits)
+    r = oracle.bf16_to_double(h_ref_bits)
+    diff = g != r
+    # fp32 accumulation vs double: the bf16 rounding of h may differ by one ulp on a few elements
+    assert diff.mean() < 0.01, f"{diff.mean():.4f} of h differ"
+    # where a dot product nearly cancels, fp32 accumulation differs from double by a
+    # small absolute amount that can exceed one ulp of the (tiny) result
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+    allowed = np.maximum(ulp * 1.01, 1e-5 * np.abs(r).max())
+    assert np.all(np.abs(g - r) <= allowed)
+
+
+@pytest.mark.parametrize("dname,T,mode,bm", [("tiny", 24, "uniform", 128), ("tiny", 300, "one_hot", 128),
+                                             ("model", 64, "uniform", 128), ("model", 700, "zipf", 128),
+                                             ("model", 200, "uniform", 37)])
+def test_grouped_gemm_swiglu(dname, T, mode, bm):
+    say("grouped gemm swiglu", dname, T, mode, bm)
+    m = gu.moe()
+    d = TINY if dname == "tiny" else MODEL
+    lay, x, ids, gr = _grouped_case(d, T, 41 + T, mode, bm)
+    dl = gu.device_layer(lay, d)
+    perm = torch.from_numpy(gr.perm).cuda()
+    h = torch.empty((T * d.top_k, d.inter), dtype=torch.int16, device="cuda")
+    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.gate_up, m.MOE_EPI_SWIGLU_BF16, x.cuda(), perm,
+                          torch.from_numpy(gr.offsets).cuda(), torch.from_numpy(gr.block_map).cuda(),
+                          torch.tensor([gr.n_tiles], dtype=torch.int32, device="cuda"), gr.block_map.shape[0], None,
+                          T, bm, h)
+    torch.cuda.synchronize()
+    ow = gu.oracle_layer(lay)
+    href = oracle.grouped_swiglu(synth.bf16_bits_numpy(x), True, d.top_k, gr.perm, gr.offsets, ow.gate_up, d.hidden,
+                                 d.inter, d.group_size)
+    _h_compare(gu.bits(h), href)
+
+
+@pytest.mark.parametrize("dname,T,mode,bm", [("tiny", 24, "uniform", 128), ("model", 64, "uniform", 128),
+                                             ("model", 700, "zipf", 128), ("model", 130, "uniform", 5)])
+def test_grouped_gemm_scatter(dname, T, mode, bm):
+    say("grouped gemm scatter", dname, T, mode, bm)
+    m = gu.moe()
+    d = TINY if dname == "tiny" else MODEL
+    lay, x, ids, gr = _grouped_case(d, T, 51 + T, mode, bm)
+    dl = gu.device_layer(lay, d)
+    ow = gu.oracle_layer(lay)
+    # the oracle's own h as the input of both sides
+    href = oracle.grouped_swiglu(synth.bf16_bits_numpy(x), True, d.top_k, gr.perm, gr.offsets, ow.gate_up, d.hidden,
+                                 d.inter, d.group_size)
+    rw = np.random.default_rng(T).uniform(0.01, 1.0, T * d.top_k).astype(np.float32)
+    y = torch.zeros((T, d.hidden), dtype=torch.float32, device="cuda")
+    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.down, m.MOE_EPI_WEIGHTED_SCATTER_F32,
+                          torch.from_numpy(href.view(np.int16)).cuda(), torch.from_numpy(gr.perm).cuda(),
+                          torch.from_numpy(gr.offsets).cuda(), torch.from_numpy(gr.block_map).cuda(),
+                          torch.tensor([gr.n_tiles], dtype=torch.int32, device="cuda"), gr.block_map.shape[0],
+                          torch.from_numpy(rw).cuda(), T, bm, y)
+    torch.cuda.synchronize()
+    o = oracle.grouped_down(href, gr.offsets, ow.down, d.hidden, d.inter, d.group_size)
+    yref = np.zeros((T, d.hidden))
+    inv = gr.inv_perm.reshape(T, d.top_k)
+    for j in range(d.top_k):
+        yref += rw.reshape(T, d.top_k)[:, j:j + 1].astype(np.float64) * o[inv[:, j]]
+    yg = y.cpu().numpy().astype(np.float64)
+    assert np.abs(yg - yref).max() <= 1e-5 * np.abs(yref).max()
+
+
+# ------------------------------------------------------------------ the whole layer
+
+@pytest.mark.parametrize("dname,T", [("tiny", 1), ("tiny", 2), ("tiny", 37), ("tiny", 129), ("model", 1),
+                                     ("model", 2), ("model", 3), ("model", 64), ("model", 127), ("model", 512)])
+def test_forward_parity_full(dname, T):
+    say("forward", dname, T)
+    d = TINY if dname == "tiny" else MODEL
+    lay = synth.make_layer(d, 61 + T)
+    x = synth.activations(T, d.hidden, 61 + T)
+    r = gu.forward_and_check(d, lay, x)
+    say("errors", r["errs"])
+
+
+@pytest.mark.parametrize("cfg", ["t4096", "skew16k"])
+def test_forward_parity_large_sampled(cfg):
+    c = synth.CONFIGS[cfg]
+    say("forward sampled", cfg, c.T)
+    lay = synth.make_layer(c.dims, c.seed, zipf_bias=c.zipf_bias)
+    x = synth.activations(c.T, c.dims.hidden, c.seed)
+    rng = np.random.default_rng(c.seed)
+    tokens = np.sort(rng.choice(c.T, 48, replace=False)).astype(np.int32)
+    tokens[0], tokens[-1] = 0, c.T - 1
+    r = gu.forward_and_check(c.dims, lay, x, tokens=tokens)
+    if c.zipf_bias:
+        counts = np.bincount(r["ids"].reshape(-1), minlength=256)
+        assert counts.max() > 10 * counts.mean() and (counts == 0).any()
+    say("errors", r["errs"])
+
+
+@pytest.mark.parametrize("cfg", ["t64", "t512"])
+def test_forward_parity_configs(cfg):
+    c = synth.CONFIGS[cfg]
+    say("forward config", cfg)
+    lay = synth.make_layer(c.dims, c.seed)
+    x = synth.activations(c.T, c.dims.hidden, c.seed)
+    r = gu.forward_and_check(c.dims, lay, x)
+    say("errors", r["errs"])
+
+
+def test_decode_layers():
+    c = synth.CONFIGS["decode"]
+    for layer in (0, 1, 39):
+        say("decode layer", layer)
+        lay = synth.make_layer(c.dims, c.seed, layer=layer)
+        for step in (0, 255):
+            x = synth.activations(1, c.dims.hidden, c.seed, step=step)
+            gu.forward_and_check(c.dims, lay, x)
+
+
+def test_forward_repeatable():
+    say("forward repeatable")
+    m = gu.moe()
+    d = MODEL
+    lay = synth.make_layer(d, 77)
+    dl = gu.device_layer(lay, d)
+    x = synth.activations(333, d.hidden, 77).cuda()
+    outs = []
+    for _ in range(3):
+        ids = torch.empty((333, d.top_k), dtype=torch.int32, device="cuda")
+        y = m.moe_forward(gu.to_dims(d), dl, x, ids_out=ids)
+        outs.append((ids, y))
+    torch.cuda.synchronize()
+    for ids, y in outs[1:]:
+        assert torch.equal(ids, outs[0][0])
+        mr, l1 = gu.out_errors(gu.bits(y), gu.bits(outs[0][1]))
+        assert mr <= 8e-3 and l1 <= 1e-4   # fp32 atomic order only
