@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-MoE layer on one MI355X.
+
+One step = one whole MoE layer (router GEMM, top-k, grouping, gate/up grouped
+GEMM with SwiGLU, down grouped GEMM with weighted scatter, combine) over one
+batch of T synthetic tokens, inputs and weights resident in HBM.
+
+Headline (``value``): prefill tokens/s of one layer at T=4096 (hidden 2048,
+256 experts top-8 + 1 shared expert, expert intermediate 512, int4 group-64
+weights).  Also reported: the layer's fraction of dense bf16 MFMA peak, the
+dominant kernel's roofline (timed live with HIP events on the launch stream),
+per-stage times, batch-1 decode over 40 stacked layers x 256 steps as HBM GB/s,
+and the CPU oracle timed on a bounded token sample of the same workload.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def layer_flops_per_token(d) -> int:
+    """MFMA-eligible flops per token: (k routed + 1 shared) experts x 3 matrices."""
+    return (d.top_k * 3 * 2 * d.hidden * d.inter) + 3 * 2 * d.hidden * d.shared_inter
+
+
+def gate_up_flops(d, T) -> int:
+    return 2 * (T * d.top_k * 2 * d.inter + T * 2 * d.shared_inter) * d.hidden
+
+
+def expert_bytes(d) -> int:
+    """int4 codes + fp16 scale + fp16 bias of one expert's three matrices."""
+    n = 3 * d.hidden * d.inter
+    return n // 2 + 2 * 2 * (n // d.group_size)
+
+
+def decode_bytes_per_layer(d) -> int:
+    shared = expert_bytes(synth_dims_shared(d))
+    return (d.top_k * expert_bytes(d) + shared + d.n_experts * d.hidden * 4 + d.hidden * 4
+            + 2 * d.hidden * 2)
+
+
+def synth_dims_shared(d):
+    import synth
+    return synth.Dims(hidden=d.hidden, inter=d.shared_inter, n_experts=1, top_k=1, group_size=d.group_size,
+                      shared_inter=d.shared_inter)
+
+
+def device_layer(lay, d, moe):
+    import torch
+    t = lambda a: None if a is None else a.to("cuda").contiguous()
+    q = lambda m: tuple(t(a) for a in m)
+    return moe.LayerWeights(moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter),
+                            q(lay.gate_up), q(lay.down), q(lay.sh_gate_up), q(lay.sh_down), t(lay.router_w),
+                            t(lay.shared_gate_w), t(lay.router_bias))
+
+
+def time_stages(moe, md, dl, x, y, ws, reps):
+    """Average GPU time (us) of each stage of the layer, HIP events on the launch stream."""
+    import torch
+    out = {}
+    for i, name in enumerate(moe.STAGES):
+        moe.moe_forward(md, dl, x, y=y, workspace=ws)        # refresh every stage's inputs
+        moe.moe_forward_stages(md, dl, x, y, ws, i, i)       # warm
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            moe.moe_forward_stages(md, dl, x, y, ws, i, i)
+        e1.record(s)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1000.0 / reps
+    moe.moe_forward(md, dl, x, y=y, workspace=ws)
+    return out
+
+
+def bench_prefill(cfg, steps, warmup):
+    import torch
+    import sparse_moe_softmax_amd as moe
+    import synth
+    d = cfg.dims
+    md = moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+    log(f"prefill {cfg.name}: generating weights (seed {cfg.seed})")
+    lay = synth.make_layer(d, cfg.seed, zipf_bias=cfg.zipf_bias, device="cuda")
+    dl = device_layer(lay, d, moe)
+    x_cpu = synth.activations(cfg.T, d.hidden, cfg.seed)
+    x = x_cpu.cuda()
+    T = cfg.T
+    ws = torch.empty(moe.moe_workspace_bytes(md, T), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, d.hidden), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((T, d.n_experts), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        moe.moe_forward(md, dl, x, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        moe.moe_forward(md, dl, x, y=y, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1000.0 / steps
+    gpu_ms = e0.elapsed_time(e1) / steps
+    log(f"prefill {cfg.name}: {wall_ms:.4f} ms/step wall, {gpu_ms:.4f} ms/step gpu events")
+    stages = time_stages(moe, md, dl, x, y, ws, reps=max(10, steps))
+    log("stages (us):", {k: round(v, 2) for k, v in stages.items()})
+    # final forward with routing outputs kept for the cross-check in the CPU leg
+    moe.moe_forward(md, dl, x, y=y, logits_out=logits, ids_out=ids, workspace=ws)
+    torch.cuda.synchronize()
+    return {"cfg": cfg, "lay": lay, "x_cpu": x_cpu, "wall_ms": wall_ms, "gpu_ms": gpu_ms, "stages": stages,
+            "y": y, "logits": logits, "ids": ids}
+
+
+def bench_decode(cfg, n_steps, graph_chunk=32):
+    import torch
+    import sparse_moe_softmax_amd as moe
+    import synth
+    d = cfg.dims
+    md = moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+    log(f"decode: generating {cfg.layers} layers (seed {cfg.seed})")
+    layers = []
+    for l in range(cfg.layers):
+        lay = synth.make_layer(d, cfg.seed, layer=l, device="cuda")
+        layers.append(device_layer(lay, d, moe))
+    xs = torch.stack([synth.activations(1, d.hidden, cfg.seed, step=s)[0] for s in range(n_steps)]).cuda()
+    ws = torch.empty(moe.moe_workspace_bytes(md, 1), dtype=torch.uint8, device="cuda")
+    ys = torch.empty((cfg.layers, d.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def step(s):
+        xi = xs[s:s + 1]
+        for l, dl in enumerate(layers):
+            moe.moe_forward(md, dl, xi, y=ys[l:l + 1], workspace=ws)
+
+    step(0)
+    torch.cuda.synchronize()
+    graphs = []
+    for c0 in range(0, n_steps, graph_chunk):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(c0, min(n_steps, c0 + graph_chunk)):
+                step(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g in graphs[:1]:
+        g.replay()                # warm
+    torch.cuda.synchronize()
+    s_ = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s_)
+    for g in graphs:
+        g.replay()
+    e1.record(s_)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gpu_s = e0.elapsed_time(e1) / 1000.0
+    bytes_step = cfg.layers * decode_bytes_per_layer(d)
+    gbs = n_steps * bytes_step / gpu_s / 1e9
+    log(f"decode: {n_steps} steps x {cfg.layers} layers in {gpu_s * 1000:.2f} ms (wall {(t1 - t0) * 1000:.2f}), "
+        f"{gbs:.1f} GB/s")
+    return {"metric": "batch-1 decode HBM GB/s (algorithmic bytes)", "value": round(gbs, 2), "unit": "GB/s",
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "us_per_step": round(gpu_s * 1e6 / n_steps, 2),
+            "us_per_layer": round(gpu_s * 1e6 / n_steps / cfg.layers, 3), "steps": n_steps, "layers": cfg.layers,
+            "bytes_per_layer": decode_bytes_per_layer(d), "launch": "HIP graphs of 32 steps",
+            "workload": "decode T=1, 40 layers distinct seeded int4 weights, fresh x per step"}
+
+
+def cpu_baseline(res, sample, threads):
+    """The oracle, as it stands, on `sample` tokens of the same workload; also
+    cross-checks those tokens' GPU outputs (shared-logits protocol)."""
+    import numpy as np
+    import oracle
+    import synth
+    cfg, lay = res["cfg"], res["lay"]
+    d = cfg.dims
+    od = oracle.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+    ln = synth.layer_numpy(lay)
+    ow = oracle.LayerWeights(ln["gate_up"], ln["down"], ln["sh_gate_up"], ln["sh_down"], ln["router_w"],
+                             ln["shared_gate_w"], ln["router_bias"])
+    rng = np.random.default_rng(cfg.seed)
+    tok = np.sort(rng.choice(cfg.T, sample, replace=False)).astype(np.int32)
+    xb = synth.bf16_bits_numpy(res["x_cpu"])[tok]
+    log(f"cpu baseline: oracle on {sample} of {cfg.T} tokens, {threads} threads")
+    t0 = time.perf_counter()
+    r = oracle.layer(od, xb, ow, threads=threads)
+    t1 = time.perf_counter()
+    secs = t1 - t0
+    # cross-check against the GPU: logits, ids given the GPU logits, and the outputs
+    g_logits = res["logits"].cpu().numpy()[tok]
+    g_ids = res["ids"].cpu().numpy()[tok]
+    logit_err = float(np.abs(g_logits - r["logits"]).max())
+    o_ids, o_w = oracle.topk(g_logits, d.top_k)
+    ids_equal = bool(np.array_equal(o_ids, g_ids))
+    out, _, _, _ = oracle.moe_tokens(od, xb, o_ids, o_w, oracle.sigmoid(r["s"]), ow, threads=threads)
+    gy = res["y"].cpu().view(__import__("torch").int16).numpy().view(np.uint16)[tok]
+    g = oracle.bf16_to_double(gy)
+    o = oracle.bf16_to_double(out)
+    max_rel = float(np.abs(g - o).max() / np.abs(o).max())
+    l1_rel = float(np.abs(g - o).sum() / np.abs(o).sum())
+    log(f"cpu baseline: {secs:.2f} s; parity max_rel {max_rel:.2e} l1_rel {l1_rel:.2e} ids_equal {ids_equal}")
+    return ({"value": round(sample / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+             "sample": f"{sample} of the {cfg.T} tokens of the same layer (router, top-k, experts incl. "
+                       f"dequantisation of the experts they touch, combine), {secs:.1f} s"},
+            {"tokens": sample, "logit_max_abs_err": logit_err, "ids_equal_given_gpu_logits": ids_equal,
+             "max_rel": max_rel, "l1_rel": l1_rel, "pass": bool(logit_err <= 1e-4 and ids_equal and
+                                                                   max_rel <= 1e-2 and l1_rel <= 2e-3)})
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="t4096", choices=["t64", "t512", "t4096", "skew16k"])
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py times the MoE layer on one GPU; --gpus {args.gpus} (world size {world}) is not "
+              f"supported: this build runs on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.workload]
+    d = cfg.dims
+    res = bench_prefill(cfg, args.steps, args.warmup)
+    T = cfg.T
+    tok_s = T / (res["wall_ms"] / 1000.0)
+    layer_tflops = layer_flops_per_token(d) * T / (res["gpu_ms"] / 1000.0) / 1e12
+    gu_us = res["stages"]["gate_up"]
+    gu_tflops = gate_up_flops(d, T) / (gu_us * 1e-6) / 1e12
+    out = {
+        "metric": "MoE-layer prefill tokens/s at T=4096 + % bf16 MFMA peak; decode HBM GB/s",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: x~N(0,1) bf16, router N(0,1/H) fp32, int4 codes uniform, fp16 scales "
+                "U(.005,.02), bias=-8*scale)",
+        "config": {"workload": f"moe_layer_prefill_{cfg.name}", "tokens": T, "hidden": d.hidden,
+                   "expert_inter": d.inter, "experts": d.n_experts, "top_k": d.top_k, "shared_experts": 1,
+                   "shared_inter": d.shared_inter, "quant": "int4 affine, group 64, fp16 scale+bias",
+                   "skewed_routing": cfg.zipf_bias, "seed": cfg.seed},
+        "layer_mfma": {"flops_per_token": layer_flops_per_token(d), "achieved_tflops": round(layer_tflops, 2),
+                       "frac_of_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+                       "gpu_ms_per_step": round(res["gpu_ms"], 5)},
+        "stages_us": {k: round(v, 2) for k, v in res["stages"].items()},
+        "roofline": {"bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_gemm_q4<0> (gate/up grouped GEMM, SwiGLU epilogue, + shared expert)",
+                     "flops_per_launch": gate_up_flops(d, T), "us_per_launch": round(gu_us, 2)},
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(synth.CONFIGS["decode"], args.decode_steps)
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        out["cpu_baseline"], out["parity_sample"] = cpu_baseline(res, args.cpu_sample, threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -174,6 +174,31 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t
                        float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* The stages of moe_forward, in order.  T > 1: router GEMM (also zeroes the
+ * fp32 combine buffer), top-k + tile histogram, grouping, gate/up grouped GEMM
+ * (+ shared expert), down grouped GEMM with weighted scatter into the fp32
+ * buffer (+ shared expert), bf16 conversion.  T == 1: ROUTER = router GEMV,
+ * GATE_UP = top-k + gate/up GEMV + SwiGLU, DOWN = down GEMV + combine + bf16;
+ * the other stages are empty. */
+typedef enum moe_stage {
+  MOE_STAGE_ROUTER = 0,
+  MOE_STAGE_TOPK = 1,
+  MOE_STAGE_GROUP = 2,
+  MOE_STAGE_GATE_UP = 3,
+  MOE_STAGE_DOWN = 4,
+  MOE_STAGE_COMBINE = 5
+} moe_stage;
+
+/* moe_forward restricted to stages first..last (inclusive).  A stage reads
+ * what the earlier stages left in `workspace`, so a range that does not start
+ * at MOE_STAGE_ROUTER needs a previous call on the same workspace, inputs and
+ * optional outputs; DOWN accumulates into the fp32 buffer that ROUTER zeroes.
+ * moe_forward() is moe_forward_stages(..., MOE_STAGE_ROUTER, MOE_STAGE_COMBINE).
+ * Lets a caller time one stage alone or interleave its own work between stages. */
+moe_status moe_forward_stages(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,
+                              float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
+                              size_t workspace_bytes, int32_t first, int32_t last, void* stream);
+
 /* Human-readable name of a status; message of the last failed check on this thread. */
 const char* moe_status_str(moe_status s);
 const char* moe_last_error_message(void);

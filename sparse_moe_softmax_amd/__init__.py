@@ -18,7 +18,8 @@ import torch  # first: libmoe then binds to the HIP runtime torch already loaded
 __all__ = [
     "Dims", "MoeError", "LayerWeights", "lib", "moe_block_m", "moe_max_tiles", "moe_prepack_router",
     "moe_router_logits", "moe_route", "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4",
-    "moe_workspace_bytes", "moe_forward", "MOE_EPI_SWIGLU_BF16", "MOE_EPI_WEIGHTED_SCATTER_F32",
+    "moe_workspace_bytes", "moe_forward", "moe_forward_stages", "MOE_EPI_SWIGLU_BF16",
+    "MOE_EPI_WEIGHTED_SCATTER_F32", "STAGES",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -26,11 +27,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32 = 0, 1
+STAGES = ("router", "topk", "group", "gate_up", "down", "combine")  # MOE_STAGE_* in order
 
 EXPORTED_SYMBOLS = (
     "moe_block_m", "moe_max_tiles", "moe_prepack_router", "moe_router_logits", "moe_route",
     "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4", "moe_workspace_bytes", "moe_forward",
-    "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
+    "moe_forward_stages", "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
 )
 
 
@@ -88,6 +90,7 @@ def lib():
                                     _I32),
             "moe_workspace_bytes": ([PD, _I32], _SZ),
             "moe_forward": ([PD, PL, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+            "moe_forward_stages": ([PD, PL, _P, _I32, _P, _P, _P, _P, _P, _SZ, _I32, _I32, _P], _I32),
             "moe_status_str": ([_I32], ctypes.c_char_p),
             "moe_last_error_message": ([], ctypes.c_char_p),
             "moe_last_hip_error": ([], _I32),
@@ -236,4 +239,15 @@ def moe_forward(d, layer: LayerWeights, x: torch.Tensor, y=None, logits_out=None
         workspace = _empty((moe_workspace_bytes(d, T),), torch.uint8, x)
     _check(lib().moe_forward(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y), _ptr(logits_out),
                              _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def moe_forward_stages(d, layer: LayerWeights, x: torch.Tensor, y: torch.Tensor, workspace: torch.Tensor,
+                       first: int, last: int, logits_out=None, ids_out=None, w_out=None) -> torch.Tensor:
+    """Stages first..last (indices into STAGES) of moe_forward on a workspace
+    filled by an earlier call with the same arguments."""
+    T = x.shape[0]
+    _check(lib().moe_forward_stages(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y),
+                                    _ptr(logits_out), _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(),
+                                    first, last, _stream()))
     return y

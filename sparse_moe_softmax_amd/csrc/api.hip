@@ -228,13 +228,15 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max) {
   return layout(*d, T_max).total;
 }
 
-moe_status moe_forward(const moe_dims* d, const moe_layer* L, const uint16_t* x, int32_t T, uint16_t* y,
-                       float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint16_t* x, int32_t T, uint16_t* y,
+                              float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
+                              size_t workspace_bytes, int32_t first, int32_t last, void* stream) {
   moe_status st = check_dims(d);
   if (st) return st;
   if ((st = check_T(T))) return st;
   if (!L || !x || !y) return fail(MOE_ERR_INVALID_ARG, "NULL layer, x or y");
+  if (first < MOE_STAGE_ROUTER || last > MOE_STAGE_COMBINE || first > last)
+    return fail(MOE_ERR_INVALID_ARG, "stage range [%d, %d] invalid", first, last);
   if ((st = check_q4(&L->gate_up, "gate_up")) || (st = check_q4(&L->down, "down")) ||
       (st = check_q4(&L->sh_gate_up, "sh_gate_up")) || (st = check_q4(&L->sh_down, "sh_down")))
     return st;
@@ -242,19 +244,22 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* L, const uint16_t* x,
   const Ws w = layout(*d, T);
   if (!workspace || workspace_bytes < w.total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, w.total);
+  if (T == 1 && !L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+  if (T > 1 && !L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = logits_out ? logits_out : at<float>(workspace, w.logits);
   int32_t* ids = ids_out ? ids_out : at<int32_t>(workspace, w.ids);
   float* wts = w_out ? w_out : at<float>(workspace, w.wts);
   float* s_logit = at<float>(workspace, w.s);
   float* gate = at<float>(workspace, w.gate);
+  auto run = [&](int stage) { return first <= stage && stage <= last; };
 
   if (T == 1) {
-    if (!L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
-    return hip_check(launch_decode(*d, *L, x, y, logits, s_logit, ids, wts, gate, at<uint16_t>(workspace, w.hdec), s),
-                     "decode");
+    DecodePtrs p{logits, s_logit, ids, wts, gate, at<uint16_t>(workspace, w.hdec)};
+    for (int stage = first; stage <= last; ++stage)
+      if ((st = hip_check(launch_decode_stage(*d, *L, x, y, p, stage, s), "decode"))) return st;
+    return MOE_OK;
   }
-  if (!L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
   float* yacc = at<float>(workspace, w.y);
   int32_t* tilehist = at<int32_t>(workspace, w.tilehist);
   int32_t* counts = at<int32_t>(workspace, w.counts);
@@ -266,22 +271,38 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* L, const uint16_t* x,
   uint16_t* hsh = at<uint16_t>(workspace, w.hsh);
   const int E = d->n_experts, k = d->top_k;
   const int mt = moe_max_tiles(T, k, E, kBM);
+  GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM))};
 
-  if ((st = hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, L->shared_gate_w, T, d->hidden, E, logits,
+  if (run(MOE_STAGE_ROUTER) &&
+      (st = hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, L->shared_gate_w, T, d->hidden, E, logits,
                                          s_logit, yacc, s),
                       "router gemm")))
     return st;
-  if ((st = hip_check(launch_topk(logits, s_logit, T, E, k, ids, wts, gate, tilehist, s), "top-k"))) return st;
-  if ((st = hip_check(launch_group(ids, tilehist, at<int32_t>(workspace, w.tilebase), T, k, E, kBM, counts, offsets,
+  if (run(MOE_STAGE_TOPK) &&
+      (st = hip_check(launch_topk(logits, s_logit, T, E, k, ids, wts, gate, tilehist, s), "top-k")))
+    return st;
+  if (run(MOE_STAGE_GROUP) &&
+      (st = hip_check(launch_group(ids, tilehist, at<int32_t>(workspace, w.tilebase), T, k, E, kBM, counts, offsets,
                                    perm, at<int32_t>(workspace, w.inv), bmap, mt, ntiles, s),
                       "grouping")))
     return st;
-  GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM))};
-  if ((st = hip_check(launch_gemm_swiglu(*d, L->gate_up, &L->sh_gate_up, x, tl, T, h, hsh, s), "gate/up gemm")))
+  if (run(MOE_STAGE_GATE_UP) &&
+      (st = hip_check(launch_gemm_swiglu(*d, L->gate_up, &L->sh_gate_up, x, tl, T, h, hsh, s), "gate/up gemm")))
     return st;
-  if ((st = hip_check(launch_gemm_scatter(*d, L->down, &L->sh_down, h, hsh, tl, wts, gate, T, yacc, s), "down gemm")))
+  if (run(MOE_STAGE_DOWN) &&
+      (st = hip_check(launch_gemm_scatter(*d, L->down, &L->sh_down, h, hsh, tl, wts, gate, T, yacc, s), "down gemm")))
     return st;
-  return hip_check(launch_finalize(yacc, y, static_cast<int64_t>(T) * d->hidden, s), "finalize");
+  if (run(MOE_STAGE_COMBINE) &&
+      (st = hip_check(launch_finalize(yacc, y, static_cast<int64_t>(T) * d->hidden, s), "finalize")))
+    return st;
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_dims* d, const moe_layer* L, const uint16_t* x, int32_t T, uint16_t* y,
+                       float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return moe_forward_stages(d, L, x, T, y, logits_out, ids_out, w_out, workspace, workspace_bytes, MOE_STAGE_ROUTER,
+                            MOE_STAGE_COMBINE, stream);
 }
 
 }  // extern "C"

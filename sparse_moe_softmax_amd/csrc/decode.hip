@@ -169,11 +169,12 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
   if (j == 0) a.y[n] = f32_to_bf16_bits(y);
 }
 
-hipError_t launch_decode(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y, float* logits,
-                         float* s_logit, int32_t* ids, float* wts, float* gate, uint16_t* h_ws, hipStream_t s) {
-  hipError_t err = launch_router_gemv(x, L.router_w, L.router_bias, L.shared_gate_w, 1, d.hidden, d.n_experts,
-                                      logits, s_logit, s);
-  if (err != hipSuccess) return err;
+hipError_t launch_decode_stage(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y,
+                               const DecodePtrs& p, int stage, hipStream_t s) {
+  if (stage == MOE_STAGE_ROUTER)
+    return launch_router_gemv(x, L.router_w, L.router_bias, L.shared_gate_w, 1, d.hidden, d.n_experts, p.logits,
+                              p.s_logit, s);
+  if (stage != MOE_STAGE_GATE_UP && stage != MOE_STAGE_DOWN) return hipSuccess;
   DecArgs a{};
   a.gu = L.gate_up;
   a.dn = L.down;
@@ -185,20 +186,21 @@ hipError_t launch_decode(const moe_dims& d, const moe_layer& L, const uint16_t* 
   a.E = d.n_experts;
   a.k = d.top_k;
   a.x = x;
-  a.logits = logits;
-  a.s_logit = s_logit;
-  a.ids = ids;
-  a.wts = wts;
-  a.gate = gate;
-  a.h = h_ws;
+  a.logits = p.logits;
+  a.s_logit = p.s_logit;
+  a.ids = p.ids;
+  a.wts = p.wts;
+  a.gate = p.gate;
+  a.h = p.h;
   a.ldh = static_cast<int>(div_up(max(d.inter, d.shared_inter), 8) * 8);
   a.y = y;
-  const int wmax = max(d.inter, d.shared_inter);
-  hipLaunchKernelGGL(k_dec_gateup, dim3(static_cast<unsigned>(div_up(wmax, 16)), d.top_k + 1), dim3(256), 0, s, a);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const size_t shbytes = static_cast<size_t>(d.top_k + 1) * a.ldh * 2;
-  hipLaunchKernelGGL(k_dec_down, dim3(static_cast<unsigned>(d.hidden / 16)), dim3(256), shbytes, s, a);
+  if (stage == MOE_STAGE_GATE_UP) {
+    const int wmax = max(d.inter, d.shared_inter);
+    hipLaunchKernelGGL(k_dec_gateup, dim3(static_cast<unsigned>(div_up(wmax, 16)), d.top_k + 1), dim3(256), 0, s, a);
+  } else {
+    const size_t shbytes = static_cast<size_t>(d.top_k + 1) * a.ldh * 2;
+    hipLaunchKernelGGL(k_dec_down, dim3(static_cast<unsigned>(d.hidden / 16)), dim3(256), shbytes, s, a);
+  }
   return hipGetLastError();
 }
 

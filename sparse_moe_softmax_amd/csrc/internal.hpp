@@ -181,8 +181,17 @@ hipError_t launch_gemm_scatter(const moe_dims& d, const moe_q4& w, const moe_q4*
                                const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate,
                                int T, float* y, hipStream_t s);
 hipError_t launch_finalize(const float* y, uint16_t* out, int64_t n, hipStream_t s);
-hipError_t launch_decode(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y, float* logits,
-                         float* s_logit, int32_t* ids, float* wts, float* gate, uint16_t* h_ws, hipStream_t s);
+struct DecodePtrs {
+  float* logits;
+  float* s_logit;
+  int32_t* ids;
+  float* wts;
+  float* gate;
+  uint16_t* h;
+};
+// One stage (MOE_STAGE_*) of the T == 1 path; stages without decode work are no-ops.
+hipError_t launch_decode_stage(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y,
+                               const DecodePtrs& p, int stage, hipStream_t s);
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

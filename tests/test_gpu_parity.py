@@ -283,3 +283,37 @@ def test_forward_repeatable():
         assert torch.equal(ids, outs[0][0])
         mr, l1 = gu.out_errors(gu.bits(y), gu.bits(outs[0][1]))
         assert mr <= 8e-3 and l1 <= 1e-4   # fp32 atomic order only
+
+
+@pytest.mark.parametrize("T", [1, 300])
+def test_graph_capture_replays(T):
+    """The layer makes no host round trip: it captures into a HIP graph, and
+    every replay (with unrelated eager work and synchronisations between
+    replays) reproduces the eager result."""
+    say("graph capture T", T)
+    m = gu.moe()
+    d = MODEL
+    lay = synth.make_layer(d, 88 + T)
+    dl = gu.device_layer(lay, d)
+    md = gu.to_dims(d)
+    x = synth.activations(T, d.hidden, 88 + T).cuda()
+    ws = torch.empty(m.moe_workspace_bytes(md, T), dtype=torch.uint8, device="cuda")
+    ids_e = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
+    y_e = m.moe_forward(md, dl, x, ids_out=ids_e, workspace=ws).clone()
+    ids_g = torch.empty_like(ids_e)
+    y_g = torch.empty_like(y_e)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.moe_forward(md, dl, x, y=y_g, ids_out=ids_g, workspace=ws)
+    a = torch.randn(512, 512, device="cuda")
+    for rep in range(4):
+        y_g.zero_()
+        ids_g.fill_(-1)
+        b = a @ a                      # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids_g, ids_e), rep
+        mr, l1 = gu.out_errors(gu.bits(y_g), gu.bits(y_e))
+        assert mr <= 8e-3 and l1 <= 1e-4, (rep, mr, l1)
+        del b
