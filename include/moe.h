@@ -139,7 +139,12 @@ typedef enum moe_epilogue {
   /* h[p][n] = bf16( silu(gate) * up ), gate/up = a_row . W_gate_up[e]^T, a_row = x[perm[p] / k] */
   MOE_EPI_SWIGLU_BF16 = 0,
   /* y[perm[p] / k][m] += row_weight[perm[p]] * (h[p] . W_down[e]^T)[m]   (fp32 atomics) */
-  MOE_EPI_WEIGHTED_SCATTER_F32 = 1
+  MOE_EPI_WEIGHTED_SCATTER_F32 = 1,
+  /* slots[t][j][m] = fp16( row_weight[f] * (h[p] . W_down[e]^T)[m] ), f = perm[p] = t*k + j:
+   * the weighted output of every routed slot, token-major [T][k+1][H] (entry j = k
+   * is the shared expert's and is left untouched).  Summing a token's entries in
+   * order gives the combine without atomics. */
+  MOE_EPI_WEIGHTED_SLOTS_F16 = 2
 } moe_epilogue;
 
 /* Grouped GEMM over the tiles of a block map with int4 weights dequantised in
@@ -152,6 +157,8 @@ typedef enum moe_epilogue {
  *            row_weight [T*k] fp32 indexed by flat slot; out = y [T][H] fp32,
  *            accumulated into (the caller zeroes it first).  Accumulation order
  *            across experts is not fixed, so y is reproducible to fp32 rounding.
+ *   SLOTS:   as SCATTER but out = slots [T][k+1][H] fp16 (see MOE_EPI_WEIGHTED_SLOTS_F16);
+ *            deterministic.
  * perm/offsets/block_map/n_tiles as produced by moe_group() with the same
  * block_m; 1 <= block_m <= moe_block_m(). */
 moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
@@ -166,8 +173,11 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
  *   y[t] = bf16( sum_j w[t][j] * E_{ids[t][j]}(x[t]) + g[t] * E_shared(x[t]) ),
  *   E(x) = ( silu(x.Wg^T) * (x.Wu^T) ) . Wd^T with the SwiGLU product rounded to bf16.
  * T == 1 runs the decode path (vector-ALU GEMV, fp32 router_w); T > 1 runs
- * router GEMM, top-k, grouping, the two grouped GEMMs and the combine on the
- * matrix cores (needs router_w3).  No host synchronisation anywhere.
+ * router GEMM, top-k, grouping, the two grouped GEMMs on the matrix cores
+ * (needs router_w3) and the combine: the down GEMM stores every slot's
+ * weighted output in fp16 and a final pass sums each token's k+1 entries in
+ * slot order (shared expert last) in fp32, so y is bitwise reproducible.
+ * No host synchronisation anywhere.
  * Optional outputs (NULL to skip): logits_out [T][E], ids_out [T][k], w_out [T][k].
  * workspace_bytes must be >= moe_workspace_bytes(d, T). */
 moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,
@@ -176,8 +186,8 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t
 
 /* The stages of moe_forward, in order.  T > 1: router GEMM (also zeroes the
  * fp32 combine buffer), top-k + tile histogram, grouping, gate/up grouped GEMM
- * (+ shared expert), down grouped GEMM with weighted scatter into the fp32
- * buffer (+ shared expert), bf16 conversion.  T == 1: ROUTER = router GEMV,
+ * (+ shared expert), down grouped GEMM writing the weighted slot outputs
+ * (+ shared expert), combine to bf16.  T == 1: ROUTER = router GEMV,
  * GATE_UP = top-k + gate/up GEMV + SwiGLU, DOWN = down GEMV + combine + bf16;
  * the other stages are empty. */
 typedef enum moe_stage {
@@ -192,7 +202,7 @@ typedef enum moe_stage {
 /* moe_forward restricted to stages first..last (inclusive).  A stage reads
  * what the earlier stages left in `workspace`, so a range that does not start
  * at MOE_STAGE_ROUTER needs a previous call on the same workspace, inputs and
- * optional outputs; DOWN accumulates into the fp32 buffer that ROUTER zeroes.
+ * optional outputs.
  * moe_forward() is moe_forward_stages(..., MOE_STAGE_ROUTER, MOE_STAGE_COMBINE).
  * Lets a caller time one stage alone or interleave its own work between stages. */
 moe_status moe_forward_stages(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,

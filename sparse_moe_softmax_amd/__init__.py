@@ -26,7 +26,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32 = 0, 1
+MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32, MOE_EPI_WEIGHTED_SLOTS_F16 = 0, 1, 2
 STAGES = ("router", "topk", "group", "gate_up", "down", "combine")  # MOE_STAGE_* in order
 
 EXPORTED_SYMBOLS = (

@@ -58,7 +58,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 // Workspace regions of moe_forward.
 struct Ws {
-  size_t logits, s, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh, y, hdec;
+  size_t logits, s, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh, slots, hdec;
   size_t total;
 };
 
@@ -90,7 +90,7 @@ Ws layout(const moe_dims& d, int32_t T) {
   w.ntiles = take(4);
   w.h = take(F * I * 2);
   w.hsh = take(static_cast<size_t>(T) * Is * 2);
-  w.y = take(static_cast<size_t>(T) * H * 4);
+  w.slots = take(static_cast<size_t>(T) * (k + 1) * H * 2);
   w.hdec = take((k + 1) * ldh * 2);
   w.total = o;
   return w;
@@ -220,6 +220,12 @@ moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue 
         launch_gemm_scatter(*d, *w, nullptr, a, nullptr, tl, row_weight, nullptr, T, static_cast<float*>(out), s),
         "grouped gemm (scatter)");
   }
+  if (epi == MOE_EPI_WEIGHTED_SLOTS_F16) {
+    if (!row_weight) return fail(MOE_ERR_INVALID_ARG, "row_weight is NULL");
+    return hip_check(
+        launch_gemm_slots(*d, *w, nullptr, a, nullptr, tl, row_weight, nullptr, T, static_cast<uint16_t*>(out), s),
+        "grouped gemm (slots)");
+  }
   return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", static_cast<int>(epi));
 }
 
@@ -260,7 +266,7 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
       if ((st = hip_check(launch_decode_stage(*d, *L, x, y, p, stage, s), "decode"))) return st;
     return MOE_OK;
   }
-  float* yacc = at<float>(workspace, w.y);
+  uint16_t* slots = at<uint16_t>(workspace, w.slots);
   int32_t* tilehist = at<int32_t>(workspace, w.tilehist);
   int32_t* counts = at<int32_t>(workspace, w.counts);
   int32_t* offsets = at<int32_t>(workspace, w.offsets);
@@ -275,7 +281,7 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
 
   if (run(MOE_STAGE_ROUTER) &&
       (st = hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, L->shared_gate_w, T, d->hidden, E, logits,
-                                         s_logit, yacc, s),
+                                         s_logit, nullptr, s),
                       "router gemm")))
     return st;
   if (run(MOE_STAGE_TOPK) &&
@@ -290,10 +296,10 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
       (st = hip_check(launch_gemm_swiglu(*d, L->gate_up, &L->sh_gate_up, x, tl, T, h, hsh, s), "gate/up gemm")))
     return st;
   if (run(MOE_STAGE_DOWN) &&
-      (st = hip_check(launch_gemm_scatter(*d, L->down, &L->sh_down, h, hsh, tl, wts, gate, T, yacc, s), "down gemm")))
+      (st = hip_check(launch_gemm_slots(*d, L->down, &L->sh_down, h, hsh, tl, wts, gate, T, slots, s), "down gemm")))
     return st;
   if (run(MOE_STAGE_COMBINE) &&
-      (st = hip_check(launch_finalize(yacc, y, static_cast<int64_t>(T) * d->hidden, s), "finalize")))
+      (st = hip_check(launch_combine(slots, y, T, d->hidden, k, s), "combine")))
     return st;
   return MOE_OK;
 }

@@ -22,7 +22,10 @@ constexpr int kWave = 64;
 
 // Tile height of the grouped GEMMs (rows of one block-map entry) and the
 // weight columns one wave owns.
-constexpr int kBM = 128;
+#ifndef MOE_BM
+#define MOE_BM 192
+#endif
+constexpr int kBM = MOE_BM;
 constexpr int kMSub = kBM / 16;     // 16-row MFMA sub-tiles per tile
 constexpr int kTopkTile = 64;       // tokens per routing tile (histogram granularity)
 
@@ -180,7 +183,12 @@ hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* 
 hipError_t launch_gemm_scatter(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
                                const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate,
                                int T, float* y, hipStream_t s);
-hipError_t launch_finalize(const float* y, uint16_t* out, int64_t n, hipStream_t s);
+// Down GEMM writing fp16 weighted slot outputs slot[t][j][:] (routed j < k, shared j = k).
+hipError_t launch_gemm_slots(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
+                             const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate, int T,
+                             uint16_t* slots, hipStream_t s);
+// out[t] = bf16( sum_j slot[t][j] ) in slot order.
+hipError_t launch_combine(const uint16_t* slots, uint16_t* out, int T, int H, int k, hipStream_t s);
 struct DecodePtrs {
   float* logits;
   float* s_logit;

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(m):
 
 
 def test_small_helpers(m):
-    assert m.moe_block_m() == 128
+    bm = m.moe_block_m()
+    assert bm % 16 == 0 and 16 <= bm <= 256
     assert m.moe_max_tiles(4096, 8, 256, 128) == 256 + 256
     assert m.moe_max_tiles(1, 8, 256, 128) == 1 + 256
     L = m.lib()
@@ -81,7 +82,7 @@ def test_bad_arguments_rejected(m):
     q = m._Q4(FAKE, FAKE, FAKE)
     g = lambda epi, bm, rw: L.moe_grouped_gemm_q4(d, ctypes.byref(q), epi, FAKE, FAKE, FAKE, FAKE, FAKE, 10, rw,
                                                   100, bm, FAKE, None)
-    assert g(0, 129, None) == -1
+    assert g(0, m.moe_block_m() + 1, None) == -1
     assert g(1, 64, None) == -1
     assert g(7, 64, FAKE) == -1
     assert "epilogue" in L.moe_last_error_message().decode()

@@ -217,6 +217,39 @@ def test_grouped_gemm_scatter(dname, T, mode, bm):
     assert np.abs(yg - yref).max() <= 1e-5 * np.abs(yref).max()
 
 
+@pytest.mark.parametrize("dname,T,mode,bm", [("tiny", 24, "uniform", 128), ("model", 64, "uniform", 128),
+                                             ("model", 700, "zipf", 128), ("model", 130, "uniform", 5)])
+def test_grouped_gemm_slots(dname, T, mode, bm):
+    """Weighted slot epilogue: slots[t][j] = fp16(w[t][j] * o) for every routed slot."""
+    say("grouped gemm slots", dname, T, mode, bm)
+    m = gu.moe()
+    d = TINY if dname == "tiny" else MODEL
+    lay, x, ids, gr = _grouped_case(d, T, 71 + T, mode, bm)
+    dl = gu.device_layer(lay, d)
+    ow = gu.oracle_layer(lay)
+    href = oracle.grouped_swiglu(synth.bf16_bits_numpy(x), True, d.top_k, gr.perm, gr.offsets, ow.gate_up, d.hidden,
+                                 d.inter, d.group_size)
+    rw = np.random.default_rng(T).uniform(0.01, 1.0, T * d.top_k).astype(np.float32)
+    k = d.top_k
+    slots = torch.full((T, k + 1, d.hidden), 0x7BFF, dtype=torch.int16, device="cuda")   # fp16 65504 marks "untouched"
+    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.down, m.MOE_EPI_WEIGHTED_SLOTS_F16,
+                          torch.from_numpy(href.view(np.int16)).cuda(), torch.from_numpy(gr.perm).cuda(),
+                          torch.from_numpy(gr.offsets).cuda(), torch.from_numpy(gr.block_map).cuda(),
+                          torch.tensor([gr.n_tiles], dtype=torch.int32, device="cuda"), gr.block_map.shape[0],
+                          torch.from_numpy(rw).cuda(), T, bm, slots)
+    torch.cuda.synchronize()
+    o = oracle.grouped_down(href, gr.offsets, ow.down, d.hidden, d.inter, d.group_size)
+    got = slots.cpu().numpy().view(np.float16).astype(np.float64)
+    ref = np.zeros((T, k, d.hidden))
+    inv = gr.inv_perm.reshape(T, k)
+    for j in range(k):
+        ref[:, j] = rw.reshape(T, k)[:, j:j + 1].astype(np.float64) * o[inv[:, j]]
+    assert np.all(got[:, k] == 65504.0)                       # the shared entry is left alone
+    err = np.abs(got[:, :k] - ref)
+    tol = np.abs(ref) * 2.0 ** -10 + 1e-5 * np.abs(ref).max()  # fp16 rounding of an fp32 result
+    assert np.all(err <= tol), float((err / np.maximum(tol, 1e-30)).max())
+
+
 # ------------------------------------------------------------------ the whole layer
 
 @pytest.mark.parametrize("dname,T", [("tiny", 1), ("tiny", 2), ("tiny", 37), ("tiny", 129), ("model", 1),
@@ -281,8 +314,7 @@ def test_forward_repeatable():
     torch.cuda.synchronize()
     for ids, y in outs[1:]:
         assert torch.equal(ids, outs[0][0])
-        mr, l1 = gu.out_errors(gu.bits(y), gu.bits(outs[0][1]))
-        assert mr <= 8e-3 and l1 <= 1e-4   # fp32 atomic order only
+        assert torch.equal(y, outs[0][1])      # fixed-order combine: bitwise reproducible
 
 
 @pytest.mark.parametrize("T", [1, 300])
@@ -314,6 +346,5 @@ def test_graph_capture_replays(T):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(ids_g, ids_e), rep
-        mr, l1 = gu.out_errors(gu.bits(y_g), gu.bits(y_e))
-        assert mr <= 8e-3 and l1 <= 1e-4, (rep, mr, l1)
+        assert torch.equal(y_g, y_e), rep
         del b
