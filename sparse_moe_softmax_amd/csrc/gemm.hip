@@ -48,15 +48,19 @@
 namespace moe {
 
 constexpr int kGemmThreads = 256;
-constexpr int kStages = 4;
-constexpr int kAStage = kBM * 128;           // bf16 [kBM][64], swizzled 16-byte chunks
 constexpr int kBStage = 256 * 32;            // int4 codes of 256 weight rows x 64 K
 constexpr int kSStage = 256 * 4;             // fp16 scale per row, zero-extended to 4 bytes
-constexpr int kStageBytes = kAStage + kBStage + 2 * kSStage;
-constexpr int kDmaPerStage = kBM / 32 + 4;   // direct loads per wave per stage
-static_assert(kStageBytes * kStages <= 160 * 1024, "LDS ring too large");
-static_assert((kStages - 2) * kDmaPerStage <= 63, "vmcnt range");
-static_assert(kStages == 4, "the wait ladder in the K loop covers 2, 1 and 0 newer stages");
+constexpr int kRingBytes = 150 * 1024;       // LDS ring shared by all stages
+// A stage holds the live rows only (MT 32-row sub-tiles, 4 KB each); the
+// ring takes as many stages as fit, at most 8.
+template <int MT>
+struct Ring {
+  static constexpr int kA = MT * 32 * 128;
+  static constexpr int kStage = kA + kBStage + 2 * kSStage;
+  static constexpr int kStages = (kRingBytes / kStage) < 8 ? (kRingBytes / kStage) : 8;
+  static_assert(kStages >= 4, "ring too shallow");
+};
+static_assert(kRingBytes + kBM * 12 <= 160 * 1024, "LDS budget");
 
 enum { kSwiglu = 0, kScatter = 1, kSlots = 2 };
 
@@ -101,6 +105,20 @@ __device__ inline uint32_t lds_addr(const void* p) {
   // wave-uniform by construction; readfirstlane puts it in an SGPR for M0
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
+// vmcnt(n * per) for a runtime n in [0, MAXN] (s_waitcnt takes an immediate).
+template <int PER, int MAXN>
+__device__ inline void wait_stages(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * PER>();
+      return;
+    }
+    wait_stages<PER, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 __device__ inline void dma16(const void* g, const void* lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
 }
@@ -108,9 +126,250 @@ __device__ inline void dma2(const void* g, const void* lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
 }
 
+// Physical 16-byte chunk of logical chunk c in row r of an A stage.  The XOR
+// key (r ^ (r >> 3)) & 7 makes the 16-byte reads of any 8 consecutive rows, and
+// of the even and of the odd rows among any 16 consecutive rows, hit distinct
+// bank groups (conflict-free for 32- and 64-bank LDS).
+__device__ inline int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// Stored position of 16-byte half h of weight row i in a B stage (row = 32 B):
+// rows are spread so that 8 (or 16) consecutive rows read distinct bank groups.
+__device__ inline int b_half(int i, int h) { return h ^ (((i >> 2) ^ (i >> 3)) & 1); }
+
+// Everything one workgroup needs once its tile and slice are known.
+struct Tile {
+  int which, row0, rows, K, N, kg, wave, lane, Ih, hc, n0;
+  bool active;
+  const uint8_t* cbase;
+  const uint16_t* sbase;
+  const uint16_t* bbase;
+};
+
+// K loop + epilogue for a tile of MT 32-row sub-tiles (straight-line code).
+//
+// MFMA v_mfma_f32_32x32x16_bf16.  Within a K block of 64 the lane group
+// g = lane/32 covers K offsets [32g, 32g+32); k-step s (0..3) of a lane holds
+// offsets 32g+8s .. 32g+8s+7 for both operands (a consistent permutation of K).
+// A fragment: row lane%32 of the sub-tile; B fragment: weight row (column)
+// lane%32 of the column group; C: acc[m][c][j] holds row 8(j/4) + 4g + (j%4),
+// column lane%32.
+template <int MODE, int MT>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsigned char* ring,
+                                          const int64_t* s_drow, const float* s_wt) {
+  constexpr int kAI = MT;                          // A direct loads per wave per stage (8 rows each)
+  constexpr int kDma = kAI + 4;                   // + 2 code loads + scale + bias
+  constexpr int kStages = Ring<MT>::kStages;
+  constexpr int kStageBytes = Ring<MT>::kStage;
+  constexpr int kAStage = Ring<MT>::kA;
+  static_assert((kStages - 2) * kDma <= 63, "vmcnt range");
+  const int wave = t.wave, lane = t.lane;
+  const int col = lane & 31, gq = lane >> 5;
+
+  // ---- per-lane sources of the direct loads.  Row indices of a gathered tile
+  //      are loaded together first (one wait), then turned into addresses.
+  const uint16_t* abase = g.a[t.which];
+  const int lda = g.lda[t.which];
+  int arow_idx[kAI];
+#pragma unroll
+  for (int j = 0; j < kAI; ++j) {
+    const int r = (wave * kAI + j) * 8 + (lane >> 3);   // tile row this lane fills
+    arow_idx[j] = t.row0 + min(r, t.rows - 1);         // padding rows re-read the last live row
+  }
+  if (MODE == kSwiglu && t.which == 0) {
+    int pr[kAI];
+#pragma unroll
+    for (int j = 0; j < kAI; ++j) pr[j] = g.perm[arow_idx[j]];
+#pragma unroll
+    for (int j = 0; j < kAI; ++j) arow_idx[j] = pr[j] / g.k;
+  }
+  int64_t asrc[kAI];   // element offsets from abase
+#pragma unroll
+  for (int j = 0; j < kAI; ++j) {
+    const int r = (wave * kAI + j) * 8 + (lane >> 3);
+    const int p = lane & 7;                            // physical chunk this lane fills
+    int c = 0;                                         // logical chunk with a_chunk(r, c) == p
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      if (a_chunk(r, cc) == p) c = cc;
+    asrc[j] = static_cast<int64_t>(arow_idx[j]) * lda + c * 8;
+  }
+  auto wr = [&](int i) -> int {
+    const int w = i >> 6, r = i & 63;
+    if (MODE == kSwiglu) {
+      const int h0 = (t.hc - wave * 32) + w * 32;
+      if (h0 >= t.Ih) return 0;
+      return (r < 32) ? h0 + r : t.Ih + h0 + (r - 32);
+    }
+    const int s0 = t.n0 - wave * 64;
+    return (s0 + w * 64 < t.N) ? s0 + i : 0;
+  };
+  const uint8_t* bsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = wave * 64 + j * 32 + (lane >> 1);
+    bsrc[j] = t.cbase + static_cast<int64_t>(wr(i)) * (t.K / 2) + b_half(i, lane & 1) * 16;
+  }
+  const int srow = wr(wave * 64 + lane);
+  const uint16_t* ssrc = t.sbase + static_cast<int64_t>(srow) * t.kg;
+  const uint16_t* zsrc = t.bbase + static_cast<int64_t>(srow) * t.kg;
+
+  auto issue = [&](int kb) {
+    unsigned char* st = ring + (kb % kStages) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kAI; ++j) dma16(abase + asrc[j] + kb * 64, st + (wave * kAI + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(bsrc[j] + kb * 32, st + kAStage + (wave * 64 + j * 32) * 32);
+    dma2(ssrc + kb, st + kAStage + kBStage + wave * 256);
+    dma2(zsrc + kb, st + kAStage + kBStage + kSStage + wave * 256);
+  };
+
+  f32x16 acc[MT][2];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[m][c][j] = 0.f;
+
+  const int kg = t.kg;
+
+  // B fragments (2 column groups x 4 k-steps) of one stage, dequantised from LDS.
+  auto dequant_stage = [&](int kb, bf16x8 (&bfr)[2][4]) {
+    const unsigned char* st = ring + (kb % kStages) * kStageBytes;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = wave * 64 + c * 32 + col;
+      const uint4 codes = *reinterpret_cast<const uint4*>(st + kAStage + i * 32 + b_half(i, gq) * 16);
+      const uint16_t sc = *reinterpret_cast<const uint16_t*>(st + kAStage + kBStage + i * 4);
+      const uint16_t bz = *reinterpret_cast<const uint16_t*>(st + kAStage + kBStage + kSStage + i * 4);
+      const DqConst dc = dq_const(sc, bz);
+      bfr[c][0] = __builtin_bit_cast(bf16x8, dequant8(codes.x, dc.s24, dc.s20, dc.bias));
+      bfr[c][1] = __builtin_bit_cast(bf16x8, dequant8(codes.y, dc.s24, dc.s20, dc.bias));
+      bfr[c][2] = __builtin_bit_cast(bf16x8, dequant8(codes.z, dc.s24, dc.s20, dc.bias));
+      bfr[c][3] = __builtin_bit_cast(bf16x8, dequant8(codes.w, dc.s24, dc.s20, dc.bias));
+    }
+  };
+
+  // One K block.  Entering iteration kb, stage kb's A tile and the dequantised
+  // B of stage kb (bcur) are ready.  The iteration waits for stage kb+1, refills
+  // the slot of stage kb-1 with stage kb+kStages-1, and overlaps the MFMAs of
+  // stage kb with the dequantisation of stage kb+1 into bnext.
+  // Every wave computes, also an idle one (narrow shared expert, or N not a
+  // multiple of the slice) on its dummy rows, whose results are never stored:
+  // a branch here would make the compiler shuttle the accumulators between
+  // register files on every K block.
+  auto iteration = [&](int kb, bf16x8 (&bcur)[2][4], bf16x8 (&bnext)[2][4]) {
+    // issued so far: stages 0 .. min(kb + kStages - 2, kg - 1); wait for stage kb+1
+    if (kb + 1 < kg) wait_stages<kDma, kStages - 3>(min(kStages - 3, kg - 2 - kb));
+    __builtin_amdgcn_s_barrier();  // stage kb+1 landed for every wave; stage kb-1 fully consumed
+    if (kb + kStages - 1 < kg) issue(kb + kStages - 1);
+    const unsigned char* st = ring + (kb % kStages) * kStageBytes;
+    if (kb + 1 < kg) dequant_stage(kb + 1, bnext);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 af[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int r = m * 32 + col;
+        af[m] = *reinterpret_cast<const bf16x8*>(st + r * 128 + (a_chunk(r, 4 * gq + ks) << 4));
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[m], bcur[c][ks], acc[m][c]);
+    }
+  };
+
+  // prologue: stages 0 .. kStages-2 in flight, stage 0 landed and dequantised
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < kg) issue(s);
+  wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1));
+  __builtin_amdgcn_s_barrier();
+  bf16x8 b0[2][4], b1[2][4];
+  dequant_stage(0, b0);
+  int kb = 0;
+  for (; kb + 1 < kg; kb += 2) {
+    iteration(kb, b0, b1);
+    iteration(kb + 1, b1, b0);
+  }
+  if (kb < kg) iteration(kb, b0, b1);
+
+  // ---- epilogue.  Each wave stages one 32-row sub-tile at a time in a private
+  // 4 KB LDS area at the start of the ring, which is free once every wave has
+  // left the loop; stores are then 16 contiguous bytes per lane.
+  __syncthreads();
+  if (!t.active) return;
+  const int rows = t.rows, row0 = t.row0;
+  unsigned char* stg = ring + wave * 4096;
+  if (MODE == kSwiglu) {
+    uint16_t* out = static_cast<uint16_t*>(g.out[t.which]);
+    const int ldo = g.ldo[t.which];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      // 32 rows x 32 h columns, bf16 (64 B per row)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float gt = acc[m][0][j];
+        const float up = acc[m][1][j];
+        const float h = gt / (1.0f + __expf(-gt)) * up;
+        const int r = (j >> 2) * 8 + gq * 4 + (j & 3);
+        reinterpret_cast<uint16_t*>(stg)[r * 32 + col] = f32_to_bf16_bits(h);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        // lane -> row 16 part + lane/4, 16-byte piece lane%4
+        const int r = part * 16 + (lane >> 2), pc = lane & 3;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + pc * 16);
+        const int rt = m * 32 + r;
+        if (rt < rows) *reinterpret_cast<uint4*>(out + static_cast<int64_t>(row0 + rt) * ldo + t.hc + pc * 8) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else if (MODE == kSlots) {
+    uint16_t* out = static_cast<uint16_t*>(g.out[0]);   // [T][k+1][H] fp16
+    const int H = g.H;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      // 32 rows x 64 columns, fp16 (128 B per row)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = (j >> 2) * 8 + gq * 4 + (j & 3);
+        const float wt = s_wt[m * 32 + r];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          reinterpret_cast<_Float16*>(stg)[r * 64 + c * 32 + col] = static_cast<_Float16>(wt * acc[m][c][j]);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+        const int r = part * 8 + (lane >> 3), pc = lane & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + pc * 16);
+        if (m * 32 + r < rows) *reinterpret_cast<uint4*>(out + s_drow[m * 32 + r] * H + t.n0 + pc * 8) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+    float* y = static_cast<float*>(g.out[t.which]);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = m * 32 + (j >> 2) * 8 + gq * 4 + (j & 3);
+        if (r < rows) {
+          float* yrow = y + s_drow[r] * g.H + t.n0 + col;
+          const float wt = s_wt[r];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) unsafeAtomicAdd(yrow + c * 32, wt * acc[m][c][j]);
+        }
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRingBytes];
 
   // ---- which tile / slice
   const int wg = blockIdx.x;
@@ -120,258 +379,80 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(GemmArgs g) {
   const int chunk = (rr / S) * 8 + xcd;
   const int slice = rr % S;
   if (chunk >= g.n_sh + g.max_tiles) return;
-  int which, e, row0, rows;
+  Tile t;
+  int e;
   if (chunk < g.n_sh) {
-    which = 1;
+    t.which = 1;
     e = 0;
-    row0 = chunk * kBM;
-    rows = min(kBM, g.T - row0);
+    t.row0 = chunk * kBM;
+    t.rows = min(kBM, g.T - t.row0);
   } else {
     const int tile = chunk - g.n_sh;
     if (tile >= *g.n_tiles) return;
-    which = 0;
+    t.which = 0;
     e = g.block_map[2 * tile];
-    row0 = g.block_map[2 * tile + 1];
-    rows = min(g.block_m, g.offsets[e + 1] - row0);
+    t.row0 = g.block_map[2 * tile + 1];
+    t.rows = min(g.block_m, g.offsets[e + 1] - t.row0);
   }
-  const int K = g.K[which];
-  const int N = g.N[which];
+  t.K = g.K[t.which];
+  t.N = g.N[t.which];
+  t.kg = t.K / 64;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 15;
-  const int q = lane >> 4;
-
-  // ---- the 256 weight rows of this slice; wave w owns rows [64w, 64w + 64) of it
-  //      (as 4 column groups of 16), `wr(i)` maps a slice row to a matrix row.
-  bool active;
-  int Ih = 0, hc = 0, n0 = 0;
+  t.lane = tid & 63;
+  t.wave = tid >> 6;
+  t.Ih = 0;
+  t.hc = 0;
+  t.n0 = 0;
   if (MODE == kSwiglu) {
-    Ih = g.Ih[which];
-    if (slice * 128 >= Ih) return;  // whole block idle (narrower shared expert)
-    hc = slice * 128 + wave * 32;
-    active = hc < Ih;
+    t.Ih = g.Ih[t.which];
+    if (slice * 128 >= t.Ih) return;  // whole block idle (narrower shared expert)
+    t.hc = slice * 128 + t.wave * 32;
+    t.active = t.hc < t.Ih;
   } else {
-    n0 = slice * 256 + wave * 64;
-    active = n0 < N;
+    t.n0 = slice * 256 + t.wave * 64;
+    t.active = t.n0 < t.N;
   }
-  // slice row i (0..255) -> matrix row; rows of idle waves map to row 0 (valid memory)
-  auto wr = [&](int i) -> int {
-    const int w = i >> 6, r = i & 63;
-    if (MODE == kSwiglu) {
-      const int h0 = slice * 128 + w * 32;
-      if (h0 >= Ih) return 0;
-      return (r < 32) ? h0 + r : Ih + h0 + (r - 32);
-    }
-    const int nn = slice * 256 + i;
-    return (slice * 256 + w * 64 < N) ? nn : 0;
-  };
-  const int kg = K / 64;
-  const uint8_t* cbase = g.codes[which] + static_cast<int64_t>(e) * N * (K / 2);
-  const uint16_t* sbase = g.scales[which] + static_cast<int64_t>(e) * N * kg;
-  const uint16_t* bbase = g.biases[which] + static_cast<int64_t>(e) * N * kg;
+  t.cbase = g.codes[t.which] + static_cast<int64_t>(e) * t.N * (t.K / 2);
+  t.sbase = g.scales[t.which] + static_cast<int64_t>(e) * t.N * t.kg;
+  t.bbase = g.biases[t.which] + static_cast<int64_t>(e) * t.N * t.kg;
 
-  // ---- per-lane sources of the direct loads (fixed for the whole K loop)
-  constexpr int kAI = kBM / 32;  // A instructions per wave per stage (8 rows each)
-  const uint16_t* abase = g.a[which];
-  const int lda = g.lda[which];
-  const uint16_t* asrc[kAI];
-#pragma unroll
-  for (int j = 0; j < kAI; ++j) {
-    const int r = (wave * kAI + j) * 8 + (lane >> 3);   // tile row this lane fills
-    const int p = lane & 7;                             // physical 16-byte chunk
-    const int c = p ^ (r & 7);                          // logical chunk it holds
-    int rsrc = (r < rows) ? r : 0;                      // padding rows load row 0 (ignored)
-    int64_t arow;
-    if (which == 1 || MODE != kSwiglu)
-      arow = row0 + rsrc;
-    else
-      arow = g.perm[row0 + rsrc] / g.k;
-    asrc[j] = abase + arow * lda + c * 8;
-  }
-  const uint8_t* bsrc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = wave * 64 + j * 32 + (lane >> 1);
-    bsrc[j] = cbase + static_cast<int64_t>(wr(i)) * (K / 2) + (lane & 1) * 16;
-  }
-  const int srow = wr(wave * 64 + lane);
-  const uint16_t* ssrc = sbase + static_cast<int64_t>(srow) * kg;
-  const uint16_t* zsrc = bbase + static_cast<int64_t>(srow) * kg;
-
-  auto issue = [&](int kb) {
-    unsigned char* st = ring + (kb % kStages) * kStageBytes;
-#pragma unroll
-    for (int j = 0; j < kAI; ++j) dma16(asrc[j] + kb * 64, st + (wave * kAI + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(bsrc[j] + kb * 32, st + kAStage + (wave * 64 + j * 32) * 32);
-    dma2(ssrc + kb, st + kAStage + kBStage + wave * 256);
-    dma2(zsrc + kb, st + kAStage + kBStage + kSStage + wave * 256);
-  };
-
-  f32x4 acc[kMSub][4];
-#pragma unroll
-  for (int m = 0; m < kMSub; ++m)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nsub = (rows + 15) >> 4;
-
-  // ---- prologue: stages 0 .. kStages-2 in flight
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < kg) issue(s);
-
-  for (int kb = 0; kb < kg; ++kb) {
-    // wait for this wave's loads of stage kb (newer stages may stay in flight)
-    const int newer = min(kStages - 2, kg - 1 - kb);
-    if (newer >= kStages - 2)
-      wait_vmcnt<(kStages - 2) * kDmaPerStage>();
-    else if (newer == 1)
-      wait_vmcnt<kDmaPerStage>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's loads of stage kb landed; stage kb-1 fully consumed
-    if (kb + kStages - 1 < kg) issue(kb + kStages - 1);
-
-    const unsigned char* st = ring + (kb % kStages) * kStageBytes;
-    if (active) {
-      // A fragments of every row sub-tile
-      bf16x8 af[kMSub][2];
-#pragma unroll
-      for (int m = 0; m < kMSub; ++m) {
-        if (m < nsub) {
-          const int r = m * 16 + col;
-          const unsigned char* rp = st + r * 128;
-          af[m][0] = *reinterpret_cast<const bf16x8*>(rp + (((2 * q) ^ (r & 7)) << 4));
-          af[m][1] = *reinterpret_cast<const bf16x8*>(rp + (((2 * q + 1) ^ (r & 7)) << 4));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = wave * 64 + c * 16 + col;
-        const uint2 codes = *reinterpret_cast<const uint2*>(st + kAStage + i * 32 + q * 8);
-        const uint16_t sc = *reinterpret_cast<const uint16_t*>(st + kAStage + kBStage + i * 4);
-        const uint16_t bz = *reinterpret_cast<const uint16_t*>(st + kAStage + kBStage + kSStage + i * 4);
-        const DqConst dc = dq_const(sc, bz);
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, dequant8(codes.x, dc.s24, dc.s20, dc.bias));
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, dequant8(codes.y, dc.s24, dc.s20, dc.bias));
-#pragma unroll
-        for (int m = 0; m < kMSub; ++m) {
-          if (m < nsub) {
-            acc[m][c] = mfma16(af[m][0], b0, acc[m][c]);
-            acc[m][c] = mfma16(af[m][1], b1, acc[m][c]);
-          }
-        }
+  // Output row and weight of every tile row (down projection epilogues), filled
+  // before the K loop; its first barrier publishes them.
+  __shared__ int64_t s_drow[kBM];
+  __shared__ float s_wt[kBM];
+  if (MODE != kSwiglu) {
+    for (int r = tid; r < t.rows; r += kGemmThreads) {
+      const int k = g.k;
+      if (t.which == 1) {
+        const int tok = t.row0 + r;
+        s_drow[r] = (MODE == kSlots) ? static_cast<int64_t>(tok) * (k + 1) + k : tok;
+        s_wt[r] = g.gate[tok];
+      } else {
+        const int f = g.perm[t.row0 + r];
+        s_drow[r] = (MODE == kSlots) ? static_cast<int64_t>(f / k) * (k + 1) + (f % k) : f / k;
+        s_wt[r] = g.row_w[f];
       }
     }
   }
-  // ---- epilogue.  C fragment: lane holds rows 4q..4q+3 of a 16-row sub-tile, column `col`.
-  // Each wave stages one 16-row sub-tile at a time in a private 2 KB LDS area
-  // at the start of the ring, which is free once every wave has left the loop.
-  __syncthreads();
-  if (!active) return;
-  unsigned char* stg = ring + wave * 2048;
-  if (MODE == kSwiglu) {
-    uint16_t* out = static_cast<uint16_t*>(g.out[which]);
-    const int ldo = g.ldo[which];
-#pragma unroll
-    for (int m = 0; m < kMSub; ++m) {
-      if (m < nsub) {
-        // 16 rows x 32 h columns, bf16 (64 B per row)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const float gt = acc[m][c][i];
-            const float up = acc[m][c + 2][i];
-            const float h = gt / (1.0f + __expf(-gt)) * up;
-            reinterpret_cast<uint16_t*>(stg)[(q * 4 + i) * 32 + c * 16 + col] = f32_to_bf16_bits(h);
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-        // lane -> row lane/4, 16-byte piece lane%4
-        const int r = lane >> 2, pc = lane & 3;
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 64 + pc * 16);
-        const int rt = m * 16 + r;
-        if (rt < rows) *reinterpret_cast<uint4*>(out + static_cast<int64_t>(row0 + rt) * ldo + hc + pc * 8) = v;
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-  } else if (MODE == kSlots) {
-    uint16_t* out = static_cast<uint16_t*>(g.out[0]);   // [T][k+1][H] fp16
-    const int H = g.H, k = g.k;
-#pragma unroll
-    for (int m = 0; m < kMSub; ++m) {
-      if (m < nsub) {
-        float wt[4];
-        int64_t orow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rt = min(m * 16 + q * 4 + i, rows - 1);
-          if (which == 1) {
-            const int t = row0 + rt;
-            wt[i] = g.gate[t];
-            orow[i] = static_cast<int64_t>(t) * (k + 1) + k;
-          } else {
-            const int f = g.perm[row0 + rt];
-            wt[i] = g.row_w[f];
-            orow[i] = static_cast<int64_t>(f / k) * (k + 1) + (f % k);
-          }
-        }
-        // 16 rows x 64 columns, fp16 (128 B per row): two halves of 8 rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const _Float16 v = static_cast<_Float16>(wt[i] * acc[m][c][i]);
-            reinterpret_cast<_Float16*>(stg)[(q * 4 + i) * 64 + c * 16 + col] = v;
-          }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int r = half * 8 + (lane >> 3), pc = lane & 7;
-          const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + pc * 16);
-          // the row's destination: held by lane with q = r/4, i = r%4
-          const int rt = m * 16 + r;
-          int64_t dst;
-          {
-            const int src_lane = (r >> 2) * 16;
-            const int ii = r & 3;
-            int64_t o0 = __shfl(orow[0], src_lane), o1 = __shfl(orow[1], src_lane);
-            int64_t o2 = __shfl(orow[2], src_lane), o3 = __shfl(orow[3], src_lane);
-            dst = ii == 0 ? o0 : ii == 1 ? o1 : ii == 2 ? o2 : o3;
-          }
-          if (rt < rows) *reinterpret_cast<uint4*>(out + dst * H + n0 + pc * 8) = v;
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-  } else {
-    float* y = static_cast<float*>(g.out[which]);
-#pragma unroll
-    for (int m = 0; m < kMSub; ++m) {
-      if (m < nsub) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = m * 16 + q * 4 + i;
-          if (r < rows) {
-            int64_t t;
-            float wt;
-            if (which == 1) {
-              t = row0 + r;
-              wt = g.gate[t];
-            } else {
-              const int f = g.perm[row0 + r];
-              t = f / g.k;
-              wt = g.row_w[f];
-            }
-            float* yrow = y + t * g.H + n0 + col;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) unsafeAtomicAdd(yrow + c * 16, wt * acc[m][c][i]);
-          }
-        }
-      }
-    }
+
+  switch ((t.rows + 31) >> 5) {
+#define MOE_MT_CASE(n) \
+  case n:              \
+    gemm_tile<MODE, n>(g, t, ring, s_drow, s_wt); \
+    break;
+    MOE_MT_CASE(1) MOE_MT_CASE(2) MOE_MT_CASE(3)
+#if MOE_BM > 96
+    MOE_MT_CASE(4)
+#endif
+#if MOE_BM > 128
+    MOE_MT_CASE(5) MOE_MT_CASE(6)
+#endif
+#if MOE_BM > 192
+    MOE_MT_CASE(7) MOE_MT_CASE(8)
+#endif
+#undef MOE_MT_CASE
+    default:
+      break;
   }
 }
 

@@ -15,6 +15,7 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -26,7 +27,7 @@ constexpr int kWave = 64;
 #define MOE_BM 192
 #endif
 constexpr int kBM = MOE_BM;
-constexpr int kMSub = kBM / 16;     // 16-row MFMA sub-tiles per tile
+static_assert(kBM % 32 == 0, "tile height: whole 32-row MFMA sub-tiles");
 constexpr int kTopkTile = 64;       // tokens per routing tile (histogram granularity)
 
 // ------------------------------------------------------------------ scalar helpers
@@ -92,6 +93,9 @@ __device__ inline DqConst dq_const(uint16_t scale_bits, uint16_t bias_bits) {
 
 __device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // ------------------------------------------------------------------ top-k (device helpers)
