@@ -27,7 +27,7 @@
  *   - Calls that share a workspace on one stream are ordered; calls that
  *     overlap on different streams must use different workspaces.
  *
- * Supported shapes: hidden % 64 == 0, inter % 32 == 0, shared_inter % 32 == 0,
+ * Supported shapes: hidden % 64 == 0, inter % 64 == 0, shared_inter % 64 == 0,
  * group_size == 64, n_experts % 16 == 0 and 16 <= n_experts <= 256,
  * 1 <= top_k <= 16 (top_k <= n_experts), 1 <= T <= 65536.
  */
@@ -64,12 +64,40 @@ typedef struct moe_dims {
  *   scales fp16  [n_exp][N][K/G], biases fp16 [n_exp][N][K/G]
  * Weight value w = bf16_rne( fp32(code) * fp32(scale) + fp32(bias) ).
  * gate_up matrices: N = 2*I (rows 0..I-1 gate, I..2I-1 up), K = H.
- * down matrices:    N = H, K = I. */
+ * down matrices:    N = H, K = I.
+ * `packed` is the same weights in the matrix-core layout written by
+ * moe_prepack_q4() (NULL if not prepared): the grouped GEMMs read only it, the
+ * T == 1 path reads only the canonical arrays. */
 typedef struct moe_q4 {
   const uint8_t* codes;
   const uint16_t* scales;
   const uint16_t* biases;
+  const uint8_t* packed;
 } moe_q4;
+
+/* Which matrix of a layer a moe_q4 holds (sets N, K and the column order). */
+typedef enum moe_matrix {
+  MOE_MAT_GATE_UP = 0,    /* routed experts: N = 2I, K = H */
+  MOE_MAT_DOWN = 1,       /* routed experts: N = H,  K = I */
+  MOE_MAT_SH_GATE_UP = 2, /* shared expert:  N = 2Is, K = H */
+  MOE_MAT_SH_DOWN = 3     /* shared expert:  N = H,  K = Is */
+} moe_matrix;
+
+/* Bytes of the matrix-core layout of n_exp experts of one matrix kind
+ * (0 for invalid arguments).  The layout: per expert, per slice of 256 product
+ * columns, per 64-wide K block, one 9216-byte block holding the 256 columns'
+ * 32 code bytes (in the order the GEMM's LDS stage uses) and then their
+ * (fp16 scale, fp16 bias) pairs; gate/up slices interleave 32 gate and the
+ * matching 32 up columns.  Columns past N are zero.  Same byte count as the
+ * canonical arrays when N is a multiple of 256 (gate/up: I of 128). */
+size_t moe_packed_q4_bytes(const moe_dims* d, int32_t matrix, int32_t n_exp);
+
+/* Rewrite canonical weights w->codes/scales/biases of n_exp experts into the
+ * matrix-core layout at `packed` (packed_bytes >= moe_packed_q4_bytes()).
+ * A one-time weight preparation, like loading the checkpoint; values are
+ * copied bit for bit, only their order changes. */
+moe_status moe_prepack_q4(const moe_dims* d, int32_t matrix, const moe_q4* w, int32_t n_exp, uint8_t* packed,
+                          size_t packed_bytes, void* stream);
 
 /* All weights of one layer. */
 typedef struct moe_layer {
@@ -159,6 +187,8 @@ typedef enum moe_epilogue {
  *            across experts is not fixed, so y is reproducible to fp32 rounding.
  *   SLOTS:   as SCATTER but out = slots [T][k+1][H] fp16 (see MOE_EPI_WEIGHTED_SLOTS_F16);
  *            deterministic.
+ * w->packed must hold the matrix-core layout of the routed experts' matrix
+ * (MOE_MAT_GATE_UP for SWIGLU, MOE_MAT_DOWN otherwise).
  * perm/offsets/block_map/n_tiles as produced by moe_group() with the same
  * block_m; 1 <= block_m <= moe_block_m(). */
 moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
@@ -174,7 +204,7 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
  *   E(x) = ( silu(x.Wg^T) * (x.Wu^T) ) . Wd^T with the SwiGLU product rounded to bf16.
  * T == 1 runs the decode path (vector-ALU GEMV, fp32 router_w); T > 1 runs
  * router GEMM, top-k, grouping, the two grouped GEMMs on the matrix cores
- * (needs router_w3) and the combine: the down GEMM stores every slot's
+ * (needs router_w3 and the packed weights of all four matrices) and the combine: the down GEMM stores every slot's
  * weighted output in fp16 and a final pass sums each token's k+1 entries in
  * slot order (shared expert last) in fp32, so y is bitwise reproducible.
  * No host synchronisation anywhere.

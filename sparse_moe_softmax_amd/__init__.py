@@ -18,7 +18,8 @@ import torch  # first: libmoe then binds to the HIP runtime torch already loaded
 __all__ = [
     "Dims", "MoeError", "LayerWeights", "lib", "moe_block_m", "moe_max_tiles", "moe_prepack_router",
     "moe_router_logits", "moe_route", "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4",
-    "moe_workspace_bytes", "moe_forward", "moe_forward_stages", "MOE_EPI_SWIGLU_BF16",
+    "moe_workspace_bytes", "moe_forward", "moe_forward_stages", "moe_packed_q4_bytes", "moe_prepack_q4",
+    "MOE_EPI_SWIGLU_BF16",
     "MOE_EPI_WEIGHTED_SCATTER_F32", "STAGES",
     "EXPORTED_SYMBOLS",
 ]
@@ -28,11 +29,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32, MOE_EPI_WEIGHTED_SLOTS_F16 = 0, 1, 2
 STAGES = ("router", "topk", "group", "gate_up", "down", "combine")  # MOE_STAGE_* in order
+MOE_MAT_GATE_UP, MOE_MAT_DOWN, MOE_MAT_SH_GATE_UP, MOE_MAT_SH_DOWN = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "moe_block_m", "moe_max_tiles", "moe_prepack_router", "moe_router_logits", "moe_route",
     "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4", "moe_workspace_bytes", "moe_forward",
     "moe_forward_stages", "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
+    "moe_packed_q4_bytes", "moe_prepack_q4",
 )
 
 
@@ -57,7 +60,8 @@ class _Dims(ctypes.Structure):
 
 
 class _Q4(ctypes.Structure):
-    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p)]
 
 
 class _Layer(ctypes.Structure):
@@ -94,6 +98,8 @@ def lib():
             "moe_status_str": ([_I32], ctypes.c_char_p),
             "moe_last_error_message": ([], ctypes.c_char_p),
             "moe_last_hip_error": ([], _I32),
+            "moe_packed_q4_bytes": ([PD, _I32, _I32], _SZ),
+            "moe_prepack_q4": ([PD, _I32, ctypes.POINTER(_Q4), _I32, _P, _SZ, _P], _I32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(h, name)
@@ -128,20 +134,28 @@ def _stream():
 
 
 def _q4(m) -> _Q4:
-    c, s, b = m
-    return _Q4(_ptr(c), _ptr(s), _ptr(b))
+    """(codes, scales, biases[, packed]) -> moe_q4."""
+    c, s, b = m[:3]
+    return _Q4(_ptr(c), _ptr(s), _ptr(b), _ptr(m[3]) if len(m) > 3 else None)
 
 
 class LayerWeights:
     """Device tensors of one layer and the C struct that points at them.
 
     gate_up/down/sh_gate_up/sh_down: (codes uint8, scales int16, biases int16)
-    in the canonical layout of ``include/moe.h``.
+    in the canonical layout of ``include/moe.h``, optionally followed by the
+    packed matrix-core layout; with ``pack=True`` (default) missing packed
+    copies are made here with moe_prepack_q4 (the T > 1 path needs them).
     """
 
     def __init__(self, d, gate_up, down, sh_gate_up, sh_down, router_w, shared_gate_w, router_bias=None,
-                 router_w3=None):
+                 router_w3=None, pack: bool = True):
         self.d = d
+        if pack:
+            gate_up, down, sh_gate_up, sh_down = (
+                m if len(m) > 3 else (*m, moe_prepack_q4(d, kind, m))
+                for kind, m in ((MOE_MAT_GATE_UP, gate_up), (MOE_MAT_DOWN, down),
+                                (MOE_MAT_SH_GATE_UP, sh_gate_up), (MOE_MAT_SH_DOWN, sh_down)))
         self.gate_up, self.down, self.sh_gate_up, self.sh_down = gate_up, down, sh_gate_up, sh_down
         self.router_w, self.shared_gate_w, self.router_bias = router_w, shared_gate_w, router_bias
         self.router_w3 = router_w3 if router_w3 is not None else moe_prepack_router(d, router_w)
@@ -168,6 +182,23 @@ def moe_prepack_router(d, router_w: torch.Tensor, router_w3: torch.Tensor | None
         router_w3 = _empty((3, d.n_experts, d.hidden), torch.int16, router_w)
     _check(lib().moe_prepack_router(ctypes.byref(_dims(d)), _ptr(router_w), _ptr(router_w3), _stream()))
     return router_w3
+
+
+def moe_packed_q4_bytes(d, matrix: int, n_exp: int) -> int:
+    return int(lib().moe_packed_q4_bytes(ctypes.byref(_dims(d)), matrix, n_exp))
+
+
+def moe_prepack_q4(d, matrix: int, w, packed: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed matrix-core layout of canonical weights w = (codes, scales, biases)."""
+    codes = w[0]
+    n_exp = codes.shape[0]
+    nb = moe_packed_q4_bytes(d, matrix, n_exp)
+    if packed is None:
+        packed = _empty((max(1, nb),), torch.uint8, codes)
+    q = _q4(w[:3])
+    _check(lib().moe_prepack_q4(ctypes.byref(_dims(d)), matrix, ctypes.byref(q), n_exp, _ptr(packed),
+                                packed.numel(), _stream()))
+    return packed
 
 
 def moe_router_logits(d, layer: LayerWeights, x: torch.Tensor, logits=None, shared_logit=None,

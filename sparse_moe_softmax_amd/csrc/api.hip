@@ -37,8 +37,8 @@ moe_status check_dims(const moe_dims* d) {
     return fail(MOE_ERR_INVALID_ARG, "dims must be positive");
   if (d->group_size != 64) return fail(MOE_ERR_UNSUPPORTED, "group_size must be 64");
   if (d->hidden % 64) return fail(MOE_ERR_UNSUPPORTED, "hidden must be a multiple of 64");
-  if (d->inter % 32 || d->shared_inter % 32)
-    return fail(MOE_ERR_UNSUPPORTED, "inter and shared_inter must be multiples of 32");
+  if (d->inter % 64 || d->shared_inter % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "inter and shared_inter must be multiples of 64");
   if (d->n_experts % 16 || d->n_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "n_experts must be 16..256, x16");
   if (d->top_k > 16 || d->top_k > d->n_experts) return fail(MOE_ERR_UNSUPPORTED, "top_k must be <= 16 and <= n_experts");
   return MOE_OK;
@@ -51,6 +51,20 @@ moe_status check_T(int32_t T) {
 
 moe_status check_q4(const moe_q4* q, const char* name) {
   if (!q || !q->codes || !q->scales || !q->biases) return fail(MOE_ERR_INVALID_ARG, "%s: NULL weight pointer", name);
+  return MOE_OK;
+}
+
+moe_status check_packed(const moe_q4* q, const char* name) {
+  if (!q || !q->packed) return fail(MOE_ERR_INVALID_ARG, "%s: packed weights are NULL (run moe_prepack_q4)", name);
+  return MOE_OK;
+}
+
+// The grouped GEMMs address activation rows with 32-bit byte offsets.
+moe_status check_gemm_extent(const moe_dims& d, int32_t T) {
+  const int64_t w = std::max(d.inter, d.shared_inter);
+  if (static_cast<int64_t>(T) * d.hidden * 2 >= (int64_t{1} << 32) ||
+      static_cast<int64_t>(T) * d.top_k * w * 2 >= (int64_t{1} << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "T=%d: activations of 4 GiB or more", T);
   return MOE_OK;
 }
 
@@ -168,6 +182,25 @@ moe_status moe_route(const moe_dims* d, const float* logits, const float* shared
                    "top-k");
 }
 
+size_t moe_packed_q4_bytes(const moe_dims* d, int32_t matrix, int32_t n_exp) {
+  if (check_dims(d) || matrix < MOE_MAT_GATE_UP || matrix > MOE_MAT_SH_DOWN || n_exp < 1) return 0;
+  return static_cast<size_t>(pack_geom(*d, matrix).expert_bytes) * static_cast<size_t>(n_exp);
+}
+
+moe_status moe_prepack_q4(const moe_dims* d, int32_t matrix, const moe_q4* w, int32_t n_exp, uint8_t* packed,
+                          size_t packed_bytes, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if (matrix < MOE_MAT_GATE_UP || matrix > MOE_MAT_SH_DOWN) return fail(MOE_ERR_INVALID_ARG, "unknown matrix %d", matrix);
+  if (n_exp < 1) return fail(MOE_ERR_INVALID_ARG, "n_exp must be positive");
+  if ((st = check_q4(w, "w"))) return st;
+  if (!packed) return fail(MOE_ERR_INVALID_ARG, "packed is NULL");
+  const size_t need = moe_packed_q4_bytes(d, matrix, n_exp);
+  if (packed_bytes < need) return fail(MOE_ERR_INVALID_ARG, "packed_bytes %zu < %zu", packed_bytes, need);
+  return hip_check(launch_prepack_q4(*d, matrix, *w, n_exp, packed, static_cast<hipStream_t>(stream)),
+                   "moe_prepack_q4");
+}
+
 size_t moe_group_workspace_bytes(const moe_dims* d, int32_t T) {
   if (check_dims(d) || check_T(T)) return 0;
   const size_t ntile = static_cast<size_t>(div_up(T, kTopkTile));
@@ -205,7 +238,8 @@ moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue 
   moe_status st = check_dims(d);
   if (st) return st;
   if ((st = check_T(T))) return st;
-  if ((st = check_q4(w, "w"))) return st;
+  if ((st = check_packed(w, "w"))) return st;
+  if ((st = check_gemm_extent(*d, T))) return st;
   if (!a || !perm || !offsets || !block_map || !n_tiles || !out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
   if (block_m < 1 || block_m > kBM) return fail(MOE_ERR_INVALID_ARG, "block_m=%d outside [1, %d]", block_m, kBM);
   if (max_tiles < 1) return fail(MOE_ERR_INVALID_ARG, "max_tiles must be positive");
@@ -243,8 +277,9 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   if (!L || !x || !y) return fail(MOE_ERR_INVALID_ARG, "NULL layer, x or y");
   if (first < MOE_STAGE_ROUTER || last > MOE_STAGE_COMBINE || first > last)
     return fail(MOE_ERR_INVALID_ARG, "stage range [%d, %d] invalid", first, last);
-  if ((st = check_q4(&L->gate_up, "gate_up")) || (st = check_q4(&L->down, "down")) ||
-      (st = check_q4(&L->sh_gate_up, "sh_gate_up")) || (st = check_q4(&L->sh_down, "sh_down")))
+  auto chk = T == 1 ? check_q4 : check_packed;   // the GEMV path reads canonical, the GEMMs packed weights
+  if ((st = chk(&L->gate_up, "gate_up")) || (st = chk(&L->down, "down")) || (st = chk(&L->sh_gate_up, "sh_gate_up")) ||
+      (st = chk(&L->sh_down, "sh_down")))
     return st;
   if (!L->shared_gate_w) return fail(MOE_ERR_INVALID_ARG, "shared_gate_w is NULL");
   const Ws w = layout(*d, T);
@@ -252,6 +287,7 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, w.total);
   if (T == 1 && !L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
   if (T > 1 && !L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
+  if (T > 1 && (st = check_gemm_extent(*d, T))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = logits_out ? logits_out : at<float>(workspace, w.logits);
   int32_t* ids = ids_out ? ids_out : at<int32_t>(workspace, w.ids);

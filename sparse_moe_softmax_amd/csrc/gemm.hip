@@ -1,35 +1,37 @@
-// Grouped expert GEMMs with int4 weights dequantised in registers
-// ("By reconstructing 4-bit weights one tile at a time within grouped GEMM
-// operations, Lily keeps the expanded arrays inside GPU registers": Inside
-// Lily page, section "Performance Gains and Workload Patterns"; prefill work
-// is matrix-matrix and belongs on the matrix units: Lily page, section "Why
-// Apple Silicon isn't just a smaller datacenter GPU").
+// Grouped expert GEMMs with int4 weights dequantised in registers.  The
+// method rebuilds the 4-bit weights one tile at a time inside the grouped GEMM,
+// so the expanded values exist only in registers and are never written back
+// (Inside Lily page, section "Performance Gains and Workload Patterns"); prefill
+// is matrix-matrix work for the matrix units (Lily page, section "Why Apple
+// Silicon isn't just a smaller datacenter GPU").
 //
 // Work unit (workgroup of 4 waves) = one tile of up to kBM rows of one expert
 // x one slice of 256 weight rows (product columns).  Tiles come from the block
 // map (routed experts) and, in the fused layer, from kBM-row chunks of the
 // shared expert, which are placed first (the largest tiles start first).
 //
+// Weights are read in the packed matrix-core layout (moe_prepack_q4): for each
+// (expert, slice, 64-wide K block) one contiguous 9216-byte block holding the
+// slice's 256 rows of codes (32 B each, already in LDS order) and their
+// (scale, bias) pairs, so that one K block of weights is nine fully used 1 KB
+// loads instead of 256 partial rows and 512 scattered 2-byte reads.
+//
 // Data path per 64-wide K block ("stage"), all asynchronous:
 //   * global -> LDS direct loads (global_load_lds, no register staging) of
-//       - the tile's activation rows, bf16 [kBM][64], rows gathered through the
+//       - the tile's activation rows, bf16 [rows][64], rows gathered through the
 //         permutation; 16-byte chunks XOR-swizzled by row so that MFMA
 //         fragment reads are bank-conflict free without padding,
-//       - the slice's int4 codes [256 rows][32 B] and fp16 scales and biases;
+//       - the weight block of the slice (codes, then scale/bias pairs);
 //   * a ring of kStages stages in LDS, refilled kStages-1 blocks ahead, with
 //     explicit vmcnt waits (every vector-memory instruction inside the loop is
 //     one of these loads, issued in a fixed order and count per stage) and one
 //     barrier per K block;
 //   * each wave reads its 64 columns' codes from LDS and dequantises them in
 //     registers into MFMA B fragments: exact fp32 c*s + b, one nearest-even
-//     rounding to bf16 (see dequant8).  Dequantised weights never reach LDS or HBM;
-//   * all A fragments of the block are loaded into registers first; then for
-//     each of the 4 column groups the B fragment is built and used by every
-//     row sub-tile, so the VALU work of the next group overlaps the MFMAs of
-//     the current one (v_mfma_f32_16x16x32_bf16, fp32 accumulators).
-// Inside a K block of 64 the lane group q = lane/16 covers K offsets
-// [16q, 16q+16) and fragment s holds 16q+8s .. +7 for both operands: a
-// consistent permutation of K, which leaves the dot products unchanged.
+//     rounding to bf16 (see dequant8), one K block ahead of the MFMAs that use
+//     them.  Dequantised weights never reach LDS or HBM;
+//   * v_mfma_f32_32x32x16_bf16 with fp32 accumulators, every A fragment used
+//     for both 32-column groups of the wave.
 //
 // Epilogues (through LDS so that every lane stores 16 contiguous bytes):
 //   SWIGLU : wave columns = 32 gate rows + the matching 32 up rows;
@@ -48,27 +50,28 @@
 namespace moe {
 
 constexpr int kGemmThreads = 256;
-constexpr int kBStage = 256 * 32;            // int4 codes of 256 weight rows x 64 K
-constexpr int kSStage = 256 * 4;             // fp16 scale per row, zero-extended to 4 bytes
-constexpr int kRingBytes = 150 * 1024;       // LDS ring shared by all stages
+constexpr int kSliceRows = 256;                  // product columns (weight rows) per slice
+constexpr int kBStage = kSliceRows * 32;         // int4 codes of 256 weight rows x 64 K
+constexpr int kPackBlock = kBStage + kSliceRows * 4;  // + (fp16 scale, fp16 bias) per row = 9216 B
+constexpr int kRingBytes = 160 * 1024 - kBM * 12 - 512;  // LDS ring shared by all stages
 // A stage holds the live rows only (MT 32-row sub-tiles, 4 KB each); the
 // ring takes as many stages as fit, at most 8.
 template <int MT>
 struct Ring {
   static constexpr int kA = MT * 32 * 128;
-  static constexpr int kStage = kA + kBStage + 2 * kSStage;
+  static constexpr int kStage = kA + kPackBlock;
   static constexpr int kStages = (kRingBytes / kStage) < 8 ? (kRingBytes / kStage) : 8;
   static_assert(kStages >= 4, "ring too shallow");
 };
 static_assert(kRingBytes + kBM * 12 <= 160 * 1024, "LDS budget");
+static_assert(kRingBytes % 256 == 0, "ring alignment");
 
 enum { kSwiglu = 0, kScatter = 1, kSlots = 2 };
 
 struct GemmArgs {
   // index 0: routed experts, 1: shared expert
-  const uint8_t* codes[2];
-  const uint16_t* scales[2];
-  const uint16_t* biases[2];
+  const uint8_t* packed[2];   // matrix-core layout
+  int64_t expert_bytes[2];    // packed bytes per expert
   int K[2];        // reduction length
   int N[2];        // weight rows per expert matrix
   int Ih[2];       // SWIGLU: intermediate width (gate rows 0..Ih-1, up rows Ih..2Ih-1)
@@ -96,14 +99,35 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Direct global -> LDS loads.  Lane i of the wave writes its bytes at
-// lds + i * 16 (16-byte form) or lds + i * 4 (2-byte form, zero-extended).
-// Issued through inline asm so that the compiler does not add its own
-// conservative vmcnt(0) wait before every later LDS read: the K loop waits for
-// exactly the stage it consumes (wait_vmcnt) and then barriers.
+// Direct global -> LDS loads through buffer instructions.  Lane i of the wave
+// writes its bytes at lds + i * 16 (16-byte form) or lds + i * 4 (4-byte form);
+// the source is the resource's base + a per-lane offset + a wave-uniform offset,
+// so that advancing a stream by one K block is a scalar add.  Issued through
+// inline asm so that the compiler does not add its own conservative vmcnt(0)
+// wait before every later LDS read: the K loop waits for exactly the stage it
+// consumes (wait_vmcnt) and then barriers.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// Raw buffer resource at `base` covering the whole 32-bit offset range
+// (num_records all ones: no range clamp; offsets are in bytes).
+__device__ inline i32x4 buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a >> 32));  // stride 0
+  r.z = -1;
+  r.w = 0x00020000;
+  return r;
+}
 __device__ inline uint32_t lds_addr(const void* p) {
-  // wave-uniform by construction; readfirstlane puts it in an SGPR for M0
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ inline void bdma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ inline void bdma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
 }
 // vmcnt(n * per) for a runtime n in [0, MAXN] (s_waitcnt takes an immediate).
 template <int PER, int MAXN>
@@ -119,13 +143,6 @@ __device__ inline void wait_stages(int n) {
   }
 }
 
-__device__ inline void dma16(const void* g, const void* lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
-}
-__device__ inline void dma2(const void* g, const void* lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
-}
-
 // Physical 16-byte chunk of logical chunk c in row r of an A stage.  The XOR
 // key (r ^ (r >> 3)) & 7 makes the 16-byte reads of any 8 consecutive rows, and
 // of the even and of the odd rows among any 16 consecutive rows, hit distinct
@@ -133,15 +150,14 @@ __device__ inline void dma2(const void* g, const void* lds) {
 __device__ inline int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 // Stored position of 16-byte half h of weight row i in a B stage (row = 32 B):
 // rows are spread so that 8 (or 16) consecutive rows read distinct bank groups.
-__device__ inline int b_half(int i, int h) { return h ^ (((i >> 2) ^ (i >> 3)) & 1); }
+// Applied once by the packing, so the stage is a plain copy of a packed block.
+__host__ __device__ inline int b_half(int i, int h) { return h ^ (((i >> 2) ^ (i >> 3)) & 1); }
 
 // Everything one workgroup needs once its tile and slice are known.
 struct Tile {
   int which, row0, rows, K, N, kg, wave, lane, Ih, hc, n0;
   bool active;
-  const uint8_t* cbase;
-  const uint16_t* sbase;
-  const uint16_t* bbase;
+  const uint8_t* pbase;   // packed blocks of this expert and slice
 };
 
 // K loop + epilogue for a tile of MT 32-row sub-tiles (straight-line code).
@@ -156,7 +172,7 @@ template <int MODE, int MT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsigned char* ring,
                                           const int64_t* s_drow, const float* s_wt) {
   constexpr int kAI = MT;                          // A direct loads per wave per stage (8 rows each)
-  constexpr int kDma = kAI + 4;                   // + 2 code loads + scale + bias
+  constexpr int kDma = kAI + 3;                   // + 2 code loads + scale/bias
   constexpr int kStages = Ring<MT>::kStages;
   constexpr int kStageBytes = Ring<MT>::kStage;
   constexpr int kAStage = Ring<MT>::kA;
@@ -181,7 +197,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
     for (int j = 0; j < kAI; ++j) arow_idx[j] = pr[j] / g.k;
   }
-  int64_t asrc[kAI];   // element offsets from abase
+  uint32_t asrc[kAI];   // byte offsets from abase (a tensor of at most 2^32 bytes)
 #pragma unroll
   for (int j = 0; j < kAI; ++j) {
     const int r = (wave * kAI + j) * 8 + (lane >> 3);
@@ -190,36 +206,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       if (a_chunk(r, cc) == p) c = cc;
-    asrc[j] = static_cast<int64_t>(arow_idx[j]) * lda + c * 8;
+    asrc[j] = (static_cast<uint32_t>(arow_idx[j]) * static_cast<uint32_t>(lda) + c * 8) * 2;
   }
-  auto wr = [&](int i) -> int {
-    const int w = i >> 6, r = i & 63;
-    if (MODE == kSwiglu) {
-      const int h0 = (t.hc - wave * 32) + w * 32;
-      if (h0 >= t.Ih) return 0;
-      return (r < 32) ? h0 + r : t.Ih + h0 + (r - 32);
-    }
-    const int s0 = t.n0 - wave * 64;
-    return (s0 + w * 64 < t.N) ? s0 + i : 0;
-  };
-  const uint8_t* bsrc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = wave * 64 + j * 32 + (lane >> 1);
-    bsrc[j] = t.cbase + static_cast<int64_t>(wr(i)) * (t.K / 2) + b_half(i, lane & 1) * 16;
-  }
-  const int srow = wr(wave * 64 + lane);
-  const uint16_t* ssrc = t.sbase + static_cast<int64_t>(srow) * t.kg;
-  const uint16_t* zsrc = t.bbase + static_cast<int64_t>(srow) * t.kg;
+  const i32x4 arsrc = buffer_rsrc(abase);
+  // weights: 2 x 1 KB of codes and 256 B of scale/bias pairs per wave and stage
+  const i32x4 brsrc = buffer_rsrc(t.pbase);
+  const uint32_t bsrc = wave * 2048 + lane * 16;
+  const uint32_t ssrc = kBStage + wave * 256 + lane * 4;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave index in a scalar register
+  const uint32_t ring_s = lds_addr(ring);
 
   auto issue = [&](int kb) {
-    unsigned char* st = ring + (kb % kStages) * kStageBytes;
+    const uint32_t st = ring_s + (kb % kStages) * kStageBytes;
+    const uint32_t aoff = kb * 128, boff = kb * kPackBlock;
 #pragma unroll
-    for (int j = 0; j < kAI; ++j) dma16(abase + asrc[j] + kb * 64, st + (wave * kAI + j) * 1024);
+    for (int j = 0; j < kAI; ++j) bdma16(arsrc, asrc[j], aoff, st + (wave_s * kAI + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(bsrc[j] + kb * 32, st + kAStage + (wave * 64 + j * 32) * 32);
-    dma2(ssrc + kb, st + kAStage + kBStage + wave * 256);
-    dma2(zsrc + kb, st + kAStage + kBStage + kSStage + wave * 256);
+    for (int j = 0; j < 2; ++j) bdma16(brsrc, bsrc + j * 1024, boff, st + kAStage + wave_s * 2048 + j * 1024);
+    bdma4(brsrc, ssrc, boff, st + kAStage + kBStage + wave_s * 256);
   };
 
   f32x16 acc[MT][2];
@@ -232,67 +236,112 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 
   const int kg = t.kg;
 
-  // B fragments (2 column groups x 4 k-steps) of one stage, dequantised from LDS.
-  auto dequant_stage = [&](int kb, bf16x8 (&bfr)[2][4]) {
+  // Codes and dequantisation constants of this wave's two 32-column groups in a stage.
+  struct BRaw {
+    uint4 codes[2];
+    DqConst dc[2];
+  };
+  auto read_b = [&](int kb, BRaw& r) {
     const unsigned char* st = ring + (kb % kStages) * kStageBytes;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int i = wave * 64 + c * 32 + col;
-      const uint4 codes = *reinterpret_cast<const uint4*>(st + kAStage + i * 32 + b_half(i, gq) * 16);
-      const uint16_t sc = *reinterpret_cast<const uint16_t*>(st + kAStage + kBStage + i * 4);
-      const uint16_t bz = *reinterpret_cast<const uint16_t*>(st + kAStage + kBStage + kSStage + i * 4);
-      const DqConst dc = dq_const(sc, bz);
-      bfr[c][0] = __builtin_bit_cast(bf16x8, dequant8(codes.x, dc.s24, dc.s20, dc.bias));
-      bfr[c][1] = __builtin_bit_cast(bf16x8, dequant8(codes.y, dc.s24, dc.s20, dc.bias));
-      bfr[c][2] = __builtin_bit_cast(bf16x8, dequant8(codes.z, dc.s24, dc.s20, dc.bias));
-      bfr[c][3] = __builtin_bit_cast(bf16x8, dequant8(codes.w, dc.s24, dc.s20, dc.bias));
+      r.codes[c] = *reinterpret_cast<const uint4*>(st + kAStage + i * 32 + b_half(i, gq) * 16);
+      const uint32_t sb = *reinterpret_cast<const uint32_t*>(st + kAStage + kBStage + i * 4);
+      r.dc[c] = dq_const(static_cast<uint16_t>(sb), static_cast<uint16_t>(sb >> 16));
+    }
+  };
+  // k-step ks of column group c: codes dword ks -> 8 bf16
+  auto dq = [&](const BRaw& r, int c, int ks) -> bf16x8 {
+    const uint32_t q = ks == 0 ? r.codes[c].x : ks == 1 ? r.codes[c].y : ks == 2 ? r.codes[c].z : r.codes[c].w;
+    return __builtin_bit_cast(bf16x8, dequant8(q, r.dc[c].s24, r.dc[c].s20, r.dc[c].bias));
+  };
+  auto read_a = [&](const unsigned char* st, int ks, bf16x8 (&af)[MT]) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int r = m * 32 + col;
+      af[m] = *reinterpret_cast<const bf16x8*>(st + r * 128 + (a_chunk(r, 4 * gq + ks) << 4));
     }
   };
 
-  // One K block.  Entering iteration kb, stage kb's A tile and the dequantised
-  // B of stage kb (bcur) are ready.  The iteration waits for stage kb+1, refills
-  // the slot of stage kb-1 with stage kb+kStages-1, and overlaps the MFMAs of
-  // stage kb with the dequantisation of stage kb+1 into bnext.
+  // One K block.  Entering iteration kb, stage kb has landed for every wave,
+  // its first A fragments are in af[0] and its dequantised weights in bcur.
+  // The iteration waits for its own loads of stage kb+1 and reads that
+  // stage's codes (a wave's codes and scales come only from its own loads, so
+  // they need no barrier), then barriers (stage kb+1 landed for every wave;
+  // stage kb-1 fully consumed), refills the slot of stage kb-1 with stage
+  // kb+kStages-1, and runs the MFMAs of stage kb while dequantising stage kb+1
+  // into bnext: the 8 dequantisations of a stage (2 column groups x 4
+  // k-steps) go one after each group of MT MFMAs, and the A fragments of the
+  // next k-step (of the next stage, after the last k-step) are read one k-step
+  // ahead; scheduling fences keep that interleaving.
+  // STEADY (kb + kStages - 1 < kg): the iteration always issues a stage and
+  // dequantises, and waits for a fixed count (one basic block).
   // Every wave computes, also an idle one (narrow shared expert, or N not a
   // multiple of the slice) on its dummy rows, whose results are never stored:
   // a branch here would make the compiler shuttle the accumulators between
   // register files on every K block.
-  auto iteration = [&](int kb, bf16x8 (&bcur)[2][4], bf16x8 (&bnext)[2][4]) {
+  bf16x8 af[2][MT];
+  auto iteration = [&](auto steady_tag, int kb, bf16x8 (&bcur)[2][4], bf16x8 (&bnext)[2][4]) {
+    constexpr bool kSteady = decltype(steady_tag)::value;
+    const bool more = kSteady || kb + 1 < kg;
     // issued so far: stages 0 .. min(kb + kStages - 2, kg - 1); wait for stage kb+1
-    if (kb + 1 < kg) wait_stages<kDma, kStages - 3>(min(kStages - 3, kg - 2 - kb));
-    __builtin_amdgcn_s_barrier();  // stage kb+1 landed for every wave; stage kb-1 fully consumed
-    if (kb + kStages - 1 < kg) issue(kb + kStages - 1);
+    if (kSteady)
+      wait_vmcnt<(kStages - 3) * kDma>();
+    else if (more)
+      wait_stages<kDma, kStages - 3>(min(kStages - 3, kg - 2 - kb));
+    BRaw raw;
+    if (more) read_b(kb + 1, raw);
+    __builtin_amdgcn_s_barrier();
+    if (kSteady || kb + kStages - 1 < kg) issue(kb + kStages - 1);
     const unsigned char* st = ring + (kb % kStages) * kStageBytes;
-    if (kb + 1 < kg) dequant_stage(kb + 1, bnext);
+    const unsigned char* st_next = ring + ((kb + 1) % kStages) * kStageBytes;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[MT];
+      if (ks < 3)
+        read_a(st, ks + 1, af[(ks + 1) & 1]);
+      else if (more)
+        read_a(st_next, 0, af[0]);
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int r = m * 32 + col;
-        af[m] = *reinterpret_cast<const bf16x8*>(st + r * 128 + (a_chunk(r, 4 * gq + ks) << 4));
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[ks & 1][m], bcur[c][ks], acc[m][c]);
+        if (more) bnext[c][ks] = dq(raw, c, ks);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[m], bcur[c][ks], acc[m][c]);
     }
   };
+  using Steady = std::integral_constant<bool, true>;
+  using Drain = std::integral_constant<bool, false>;
 
-  // prologue: stages 0 .. kStages-2 in flight, stage 0 landed and dequantised
+  // prologue: stages 0 .. kStages-2 in flight, stage 0 landed, dequantised and
+  // its first A fragments read
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
     if (s < kg) issue(s);
   wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1));
   __builtin_amdgcn_s_barrier();
   bf16x8 b0[2][4], b1[2][4];
-  dequant_stage(0, b0);
-  int kb = 0;
-  for (; kb + 1 < kg; kb += 2) {
-    iteration(kb, b0, b1);
-    iteration(kb + 1, b1, b0);
+  {
+    BRaw raw;
+    read_b(0, raw);
+    read_a(ring, 0, af[0]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) b0[c][ks] = dq(raw, c, ks);
   }
-  if (kb < kg) iteration(kb, b0, b1);
+  int kb = 0;
+  const int steady_end = kg - (kStages - 1);   // iterations kb < steady_end are steady
+  for (; kb + 2 <= steady_end; kb += 2) {
+    iteration(Steady{}, kb, b0, b1);
+    iteration(Steady{}, kb + 1, b1, b0);
+  }
+  for (; kb + 2 <= kg; kb += 2) {
+    iteration(Drain{}, kb, b0, b1);
+    iteration(Drain{}, kb + 1, b1, b0);
+  }
+  if (kb < kg) iteration(Drain{}, kb, b0, b1);
 
   // ---- epilogue.  Each wave stages one 32-row sub-tile at a time in a private
   // 4 KB LDS area at the start of the ring, which is free once every wave has
@@ -311,7 +360,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
       for (int j = 0; j < 16; ++j) {
         const float gt = acc[m][0][j];
         const float up = acc[m][1][j];
-        const float h = gt / (1.0f + __expf(-gt)) * up;
+        const float h = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
         const int r = (j >> 2) * 8 + gq * 4 + (j & 3);
         reinterpret_cast<uint16_t*>(stg)[r * 32 + col] = f32_to_bf16_bits(h);
       }
@@ -412,9 +461,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(GemmArgs g) {
     t.n0 = slice * 256 + t.wave * 64;
     t.active = t.n0 < t.N;
   }
-  t.cbase = g.codes[t.which] + static_cast<int64_t>(e) * t.N * (t.K / 2);
-  t.sbase = g.scales[t.which] + static_cast<int64_t>(e) * t.N * t.kg;
-  t.bbase = g.biases[t.which] + static_cast<int64_t>(e) * t.N * t.kg;
+  t.pbase = g.packed[t.which] + static_cast<int64_t>(e) * g.expert_bytes[t.which] +
+            static_cast<int64_t>(slice) * t.kg * kPackBlock;
 
   // Output row and weight of every tile row (down projection epilogues), filled
   // before the K loop; its first barrier publishes them.
@@ -474,9 +522,8 @@ static void fill_common(GemmArgs& g, const moe_dims& d, const GemmTiles& tl, int
 hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* x,
                               const GemmTiles& tl, int T, uint16_t* h, uint16_t* h_sh, hipStream_t s) {
   GemmArgs g{};
-  g.codes[0] = w.codes;
-  g.scales[0] = w.scales;
-  g.biases[0] = w.biases;
+  g.packed[0] = w.packed;
+  g.expert_bytes[0] = pack_geom(d, MOE_MAT_GATE_UP).expert_bytes;
   g.K[0] = d.hidden;
   g.N[0] = 2 * d.inter;
   g.Ih[0] = d.inter;
@@ -485,9 +532,8 @@ hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* 
   g.out[0] = h;
   g.ldo[0] = d.inter;
   if (w_sh) {
-    g.codes[1] = w_sh->codes;
-    g.scales[1] = w_sh->scales;
-    g.biases[1] = w_sh->biases;
+    g.packed[1] = w_sh->packed;
+    g.expert_bytes[1] = pack_geom(d, MOE_MAT_SH_GATE_UP).expert_bytes;
     g.K[1] = d.hidden;
     g.N[1] = 2 * d.shared_inter;
     g.Ih[1] = d.shared_inter;
@@ -508,9 +554,8 @@ static GemmArgs down_args(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh
                           const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate, int T,
                           void* out) {
   GemmArgs g{};
-  g.codes[0] = w.codes;
-  g.scales[0] = w.scales;
-  g.biases[0] = w.biases;
+  g.packed[0] = w.packed;
+  g.expert_bytes[0] = pack_geom(d, MOE_MAT_DOWN).expert_bytes;
   g.K[0] = d.inter;
   g.N[0] = d.hidden;
   g.a[0] = h;
@@ -518,9 +563,8 @@ static GemmArgs down_args(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh
   g.out[0] = out;
   g.ldo[0] = d.hidden;
   if (w_sh) {
-    g.codes[1] = w_sh->codes;
-    g.scales[1] = w_sh->scales;
-    g.biases[1] = w_sh->biases;
+    g.packed[1] = w_sh->packed;
+    g.expert_bytes[1] = pack_geom(d, MOE_MAT_SH_DOWN).expert_bytes;
     g.K[1] = d.shared_inter;
     g.N[1] = d.hidden;
     g.a[1] = h_sh;
@@ -550,6 +594,52 @@ hipError_t launch_gemm_slots(const moe_dims& d, const moe_q4& w, const moe_q4* w
   GemmArgs g = down_args(d, w, w_sh, h, h_sh, tl, row_w, gate, T, slots);
   const int grid = gemm_grid(g.n_sh + g.max_tiles, g.n_slices);
   hipLaunchKernelGGL(k_gemm_q4<kSlots>, dim3(grid), dim3(kGemmThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+// Canonical -> packed weights: one thread per (expert, slice, K block, packed
+// row) copies the row's 32 code bytes of the block into its LDS-order position
+// and its (scale, bias) pair.  Rows past the matrix are zero.
+__global__ __launch_bounds__(256) void k_prepack_q4(const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ scales,
+                                                    const uint16_t* __restrict__ biases, uint8_t* __restrict__ packed,
+                                                    PackGeom pg) {
+  const int i = threadIdx.x;                 // packed row in the slice
+  const int64_t blk = blockIdx.x;            // ((e * slices) + s) * kg + kb
+  const int kb = static_cast<int>(blk % pg.kg);
+  const int sl = static_cast<int>((blk / pg.kg) % pg.slices);
+  const int64_t e = blk / (static_cast<int64_t>(pg.kg) * pg.slices);
+  int n;
+  if (pg.swiglu) {
+    const int w = i >> 6, r = i & 63;
+    const int hcol = sl * 128 + w * 32 + (r & 31);
+    n = hcol < pg.Iw ? ((r < 32) ? hcol : pg.Iw + hcol) : -1;
+  } else {
+    n = sl * kSliceRows + i;
+    n = n < pg.N ? n : -1;
+  }
+  uint8_t* out = packed + e * pg.expert_bytes + blk % (static_cast<int64_t>(pg.kg) * pg.slices) * kPackBlock;
+  uint4 c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
+  uint32_t sb = 0;
+  if (n >= 0) {
+    const uint8_t* src = codes + (e * pg.N + n) * (pg.K / 2) + kb * 32;
+    c0 = *reinterpret_cast<const uint4*>(src);
+    c1 = *reinterpret_cast<const uint4*>(src + 16);
+    const int64_t gi = (e * pg.N + n) * pg.kg + kb;
+    sb = static_cast<uint32_t>(scales[gi]) | (static_cast<uint32_t>(biases[gi]) << 16);
+  }
+  *reinterpret_cast<uint4*>(out + i * 32 + b_half(i, 0) * 16) = c0;
+  *reinterpret_cast<uint4*>(out + i * 32 + b_half(i, 1) * 16) = c1;
+  *reinterpret_cast<uint32_t*>(out + kBStage + i * 4) = sb;
+}
+
+hipError_t launch_prepack_q4(const moe_dims& d, int matrix, const moe_q4& w, int n_exp, uint8_t* packed,
+                             hipStream_t s) {
+  const PackGeom pg = pack_geom(d, matrix);
+  const int64_t blocks = static_cast<int64_t>(n_exp) * pg.slices * pg.kg;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prepack_q4, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, w.codes, w.scales,
+                     w.biases, packed, pg);
   return hipGetLastError();
 }
 

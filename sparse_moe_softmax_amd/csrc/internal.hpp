@@ -1,5 +1,5 @@
 // Internal declarations shared by the HIP translation units of libmoe.
-// Written for gfx950 (CDNA4): 64-lane wavefronts, bf16 MFMA 16x16x32.
+// Written for gfx950 (CDNA4): 64-lane wavefronts, bf16 MFMA.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -171,6 +171,35 @@ struct GemmTiles {
   int32_t n_shared_chunks;   // shared-expert tiles of kBM rows put first (0 = none)
 };
 
+// Geometry of the packed (matrix-core) layout of one expert matrix: slices of
+// 256 product columns x K blocks of 64, 9216 bytes per (slice, K block).
+struct PackGeom {
+  int N, K, Iw;       // canonical rows, reduction length, SwiGLU width (gate/up kinds)
+  int slices, kg;     // slices per expert, K blocks
+  bool swiglu;        // gate/up column order (32 gate + 32 up per wave)
+  int64_t expert_bytes;
+};
+inline PackGeom pack_geom(const moe_dims& d, int matrix) {
+  PackGeom g{};
+  const bool sh = matrix == MOE_MAT_SH_GATE_UP || matrix == MOE_MAT_SH_DOWN;
+  g.Iw = sh ? d.shared_inter : d.inter;
+  g.swiglu = matrix == MOE_MAT_GATE_UP || matrix == MOE_MAT_SH_GATE_UP;
+  if (g.swiglu) {
+    g.N = 2 * g.Iw;
+    g.K = d.hidden;
+    g.slices = static_cast<int>((g.Iw + 127) / 128);
+  } else {
+    g.N = d.hidden;
+    g.K = g.Iw;
+    g.slices = static_cast<int>((d.hidden + 255) / 256);
+  }
+  g.kg = g.K / 64;
+  g.expert_bytes = static_cast<int64_t>(g.slices) * g.kg * 9216;
+  return g;
+}
+
+hipError_t launch_prepack_q4(const moe_dims& d, int matrix, const moe_q4& w, int n_exp, uint8_t* packed,
+                             hipStream_t s);
 hipError_t launch_prepack_router(const float* w, uint16_t* w3, int E, int H, hipStream_t s);
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w3, const float* bias, const float* wsg, int T,
                               int H, int E, float* logits, float* s_logit, float* y_zero, hipStream_t s);

@@ -53,7 +53,8 @@ FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails valid
 
 
 @pytest.mark.parametrize("kw,status", [
-    ({"group_size": 32}, -2), ({"hidden": 96}, -2), ({"inter": 48}, -2), ({"n_experts": 512}, -2),
+    ({"group_size": 32}, -2), ({"hidden": 96}, -2), ({"inter": 48}, -2), ({"inter": 96}, -2),
+    ({"shared_inter": 160}, -2), ({"n_experts": 512}, -2),
     ({"n_experts": 24}, -2), ({"top_k": 17}, -2), ({"top_k": 0}, -1), ({"hidden": -64}, -1)])
 def test_bad_dims_rejected(m, kw, status):
     L = m.lib()
@@ -79,7 +80,7 @@ def test_bad_arguments_rejected(m):
     assert L.moe_group(*args(0, mt, need)) == -1
     assert L.moe_group(*args(64, mt, need - 1)) == -3
     # grouped gemm: block_m above the kernel tile, scatter without weights, unknown epilogue
-    q = m._Q4(FAKE, FAKE, FAKE)
+    q = m._Q4(FAKE, FAKE, FAKE, FAKE)
     g = lambda epi, bm, rw: L.moe_grouped_gemm_q4(d, ctypes.byref(q), epi, FAKE, FAKE, FAKE, FAKE, FAKE, 10, rw,
                                                   100, bm, FAKE, None)
     assert g(0, m.moe_block_m() + 1, None) == -1
@@ -93,7 +94,7 @@ def test_forward_workspace_checked(m):
     d = _d(m)
     need = L.moe_workspace_bytes(d, 4096)
     assert need > L.moe_workspace_bytes(d, 64) > 0
-    q = m._Q4(FAKE, FAKE, FAKE)
+    q = m._Q4(FAKE, FAKE, FAKE, FAKE)
     layer = m._Layer(q, q, q, q, FAKE, None, FAKE, FAKE)
     assert L.moe_forward(d, ctypes.byref(layer), FAKE, 4096, FAKE, None, None, None, FAKE, need - 1, None) == -3
     assert L.moe_forward(d, ctypes.byref(layer), FAKE, 4096, FAKE, None, None, None, None, need, None) == -3
@@ -101,6 +102,31 @@ def test_forward_workspace_checked(m):
     assert L.moe_forward(d, ctypes.byref(nolayer), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
     nor3 = m._Layer(q, q, q, q, FAKE, None, FAKE, None)
     assert L.moe_forward(d, ctypes.byref(nor3), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
+    unpacked = m._Q4(FAKE, FAKE, FAKE, None)
+    nopack = m._Layer(unpacked, q, q, q, FAKE, None, FAKE, FAKE)
+    assert L.moe_forward(d, ctypes.byref(nopack), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
+    assert "moe_prepack_q4" in L.moe_last_error_message().decode()
+    # the T == 1 path reads only the canonical arrays
+    nocanon = m._Layer(m._Q4(None, None, None, FAKE), q, q, q, FAKE, None, FAKE, FAKE)
+    assert L.moe_forward(d, ctypes.byref(nocanon), FAKE, 1, FAKE, None, None, None, FAKE, need, None) == -1
+
+
+def test_packed_sizes_and_checks(m):
+    L = m.lib()
+    d = _d(m)
+    # 256-column slices x 64-wide K blocks x 9216 B: the canonical byte count for these dims
+    canon = lambda N, K: N * K // 2 + 2 * N * (K // 64) * 2
+    assert L.moe_packed_q4_bytes(d, m.MOE_MAT_GATE_UP, 256) == 256 * canon(1024, 2048)
+    assert L.moe_packed_q4_bytes(d, m.MOE_MAT_DOWN, 256) == 256 * canon(2048, 512)
+    assert L.moe_packed_q4_bytes(d, m.MOE_MAT_SH_GATE_UP, 1) == canon(1024, 2048)
+    assert L.moe_packed_q4_bytes(_d(m, shared_inter=192), m.MOE_MAT_SH_GATE_UP, 1) == 2 * 32 * 9216  # padded slice
+    assert L.moe_packed_q4_bytes(d, 4, 1) == 0 and L.moe_packed_q4_bytes(d, 0, 0) == 0
+    q = m._Q4(FAKE, FAKE, FAKE, None)
+    need = L.moe_packed_q4_bytes(d, 0, 2)
+    assert L.moe_prepack_q4(d, 0, ctypes.byref(q), 2, FAKE, need - 1, None) == -1
+    assert L.moe_prepack_q4(d, 5, ctypes.byref(q), 2, FAKE, need, None) == -1
+    assert L.moe_prepack_q4(d, 0, ctypes.byref(m._Q4(None, FAKE, FAKE, None)), 2, FAKE, need, None) == -1
+    assert L.moe_prepack_q4(_d(m, inter=96), 0, ctypes.byref(q), 2, FAKE, need, None) == -2
 
 
 def test_binding_refuses_host_tensors(m):

@@ -49,6 +49,60 @@ def test_prepack_router_is_exact_split():
     assert torch.equal(planes.sum(0), W.to(torch.float64))
 
 
+def _pack_reference(codes, scales, biases, swiglu, Iw, N, K):
+    """The packed layout written out with numpy loops over blocks: per expert,
+    slice of 256 columns and K block of 64, 256 rows x 32 code bytes (the two
+    16-byte halves of row i swapped when bit 0 of (i >> 2) ^ (i >> 3) is set),
+    then 256 (scale, bias) fp16 pairs; gate/up slices hold, per 64 rows, 32 gate
+    rows and the 32 up rows of the same intermediate columns; missing rows zero."""
+    n_exp = codes.shape[0]
+    kg = K // 64
+    slices = -(-Iw // 128) if swiglu else -(-N // 256)
+    out = np.zeros((n_exp, slices, kg, 9216), dtype=np.uint8)
+    i = np.arange(256)
+    if swiglu:
+        hcol = (i >> 6) * 32 + (i & 31)
+        up = (i & 63) >= 32
+    for sl in range(slices):
+        if swiglu:
+            hc = sl * 128 + hcol
+            rows = np.where(hc < Iw, np.where(up, Iw + hc, hc), -1)
+        else:
+            rows = sl * 256 + i
+            rows = np.where(rows < N, rows, -1)
+        ok = rows >= 0
+        swap = (((i >> 2) ^ (i >> 3)) & 1).astype(bool)
+        for kb in range(kg):
+            blk = np.zeros((n_exp, 256, 32), dtype=np.uint8)
+            blk[:, ok] = codes[:, rows[ok], kb * 32:(kb + 1) * 32]
+            blk[:, swap] = np.concatenate([blk[:, swap, 16:], blk[:, swap, :16]], axis=2)
+            sb = np.zeros((n_exp, 256, 2), dtype=np.uint16)
+            sb[:, ok, 0] = scales[:, rows[ok], kb]
+            sb[:, ok, 1] = biases[:, rows[ok], kb]
+            out[:, sl, kb, :8192] = blk.reshape(n_exp, -1)
+            out[:, sl, kb, 8192:] = sb.reshape(n_exp, -1).view(np.uint8)
+    return out.reshape(n_exp, -1)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+def test_prepack_q4_layout(kind):
+    say("prepack q4 kind", kind)
+    m = gu.moe()
+    d = synth.Dims(hidden=512, inter=192, n_experts=16, top_k=4, group_size=64, shared_inter=320)
+    Iw = d.shared_inter if kind >= 2 else d.inter
+    swiglu = kind in (0, 2)
+    N, K = (2 * Iw, d.hidden) if swiglu else (d.hidden, Iw)
+    n_exp = 3 if kind < 2 else 1
+    w = synth.q4_matrix(n_exp, N, K, 64, seed=11, layer=kind, matrix="gate_up" if swiglu else "down", device="cuda")
+    packed = m.moe_prepack_q4(gu.to_dims(d), kind, w)
+    torch.cuda.synchronize()
+    c, sc, bi = (a.cpu().numpy() for a in w)
+    ref = _pack_reference(c, sc.view(np.uint16), bi.view(np.uint16), swiglu, Iw, N, K)
+    got = packed.cpu().numpy().reshape(n_exp, -1)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
 # ------------------------------------------------------------------ router logits
 
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 300])
