@@ -124,7 +124,7 @@ int32_t moe_max_tiles(int32_t T, int32_t top_k, int32_t n_experts, int32_t block
  * A one-time weight preparation, like loading the checkpoint. */
 moe_status moe_prepack_router(const moe_dims* d, const float* router_w, uint16_t* router_w3, void* stream);
 
-/* Router logits (step: "a router scores 256 expert subnetworks", Lily page,
+/* Router logits: every token is scored against every routed expert (Lily page,
  * section "The architecture that forces the issue: MoE plus Gated DeltaNet").
  *   x [T][H] bf16 -> logits [T][E] fp32 = x . router_w^T (+ router_bias),
  *                    shared_logit [T] fp32 = x . shared_gate_w  (NULL to skip).
@@ -147,9 +147,9 @@ moe_status moe_route(const moe_dims* d, const float* logits, const float* shared
 /* Scratch bytes moe_group() needs for T tokens. */
 size_t moe_group_workspace_bytes(const moe_dims* d, int32_t T);
 
-/* GPU-resident grouping of the T*k routed slots by expert ("Routing histograms
- * and block maps remain inside GPU command buffers", Inside Lily page, section
- * "Performance Gains and Workload Patterns").  Flat slot f = t*k + j.
+/* GPU-resident grouping of the T*k routed slots by expert: histogram and block
+ * map never leave the GPU (Inside Lily page, section "Performance Gains and
+ * Workload Patterns").  Flat slot f = t*k + j.
  *   counts   [E]      slots per expert (sum = T*k)
  *   offsets  [E+1]    exclusive prefix sum of counts, offsets[E] = T*k
  *   perm     [T*k]    slots grouped by expert; within an expert ascending f (stable)
@@ -176,9 +176,9 @@ typedef enum moe_epilogue {
 } moe_epilogue;
 
 /* Grouped GEMM over the tiles of a block map with int4 weights dequantised in
- * registers (bf16 matrix cores, fp32 accumulation; "reconstructing 4-bit
- * weights one tile at a time within grouped GEMM operations", Inside Lily page,
- * section "Performance Gains and Workload Patterns").  Routed experts only.
+ * registers, tile by tile inside the GEMM (bf16 matrix cores, fp32
+ * accumulation; Inside Lily page, section "Performance Gains and Workload
+ * Patterns").  Routed experts only.
  *   SWIGLU:  a = x [T][H] bf16 (token rows, gathered through perm);
  *            w = gate_up weights; out = h [T*k][I] bf16 in grouped order.
  *   SCATTER: a = h [T*k][I] bf16 in grouped order; w = down weights;

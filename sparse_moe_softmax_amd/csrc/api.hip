@@ -72,7 +72,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 // Workspace regions of moe_forward.
 struct Ws {
-  size_t logits, s, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh, slots, hdec;
+  size_t logits, s, rparts, sparts, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh,
+      slots, hdec;
+  int splits;
   size_t total;
 };
 
@@ -91,6 +93,9 @@ Ws layout(const moe_dims& d, int32_t T) {
   };
   w.logits = take(T * E * 4);
   w.s = take(T * 4);
+  w.splits = T > 1 ? router_splits(T, d.hidden, d.n_experts) : 1;
+  w.rparts = take(w.splits > 1 ? w.splits * T * E * 4 : 0);
+  w.sparts = take(w.splits > 1 ? w.splits * T * 4 : 0);
   w.ids = take(F * 4);
   w.wts = take(F * 4);
   w.gate = take(T * 4);
@@ -165,7 +170,7 @@ moe_status moe_router_logits(const moe_dims* d, const moe_layer* L, const uint16
   }
   if (!L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
   return hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, shared_logit ? L->shared_gate_w : nullptr, T,
-                                      d->hidden, d->n_experts, logits, shared_logit, nullptr, s),
+                                      d->hidden, d->n_experts, 1, logits, shared_logit, s),
                    "router gemm");
 }
 
@@ -177,8 +182,8 @@ moe_status moe_route(const moe_dims* d, const float* logits, const float* shared
   if (!logits || !ids || !weights) return fail(MOE_ERR_INVALID_ARG, "NULL logits, ids or weights");
   if ((gate != nullptr) != (shared_logit != nullptr))
     return fail(MOE_ERR_INVALID_ARG, "shared_logit and gate must both be given or both be NULL");
-  return hip_check(launch_topk(logits, shared_logit, T, d->n_experts, d->top_k, ids, weights, gate, nullptr,
-                               static_cast<hipStream_t>(stream)),
+  return hip_check(launch_topk(logits, shared_logit, 1, nullptr, T, d->n_experts, d->top_k, nullptr, nullptr, ids,
+                               weights, gate, nullptr, static_cast<hipStream_t>(stream)),
                    "top-k");
 }
 
@@ -315,13 +320,18 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   const int mt = moe_max_tiles(T, k, E, kBM);
   GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM))};
 
+  // router output: final logits (one K split) or per-split partial sums that top-k adds up in order
+  const int S = w.splits;
+  float* rout = S > 1 ? at<float>(workspace, w.rparts) : logits;
+  float* sout = S > 1 ? at<float>(workspace, w.sparts) : s_logit;
   if (run(MOE_STAGE_ROUTER) &&
-      (st = hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, L->shared_gate_w, T, d->hidden, E, logits,
-                                         s_logit, nullptr, s),
+      (st = hip_check(launch_router_gemm(x, L->router_w3, L->router_bias, L->shared_gate_w, T, d->hidden, E, S, rout,
+                                         sout, s),
                       "router gemm")))
     return st;
   if (run(MOE_STAGE_TOPK) &&
-      (st = hip_check(launch_topk(logits, s_logit, T, E, k, ids, wts, gate, tilehist, s), "top-k")))
+      (st = hip_check(launch_topk(rout, sout, S, L->router_bias, T, E, k, logits, s_logit, ids, wts, gate, tilehist, s),
+                      "top-k")))
     return st;
   if (run(MOE_STAGE_GROUP) &&
       (st = hip_check(launch_group(ids, tilehist, at<int32_t>(workspace, w.tilebase), T, k, E, kBM, counts, offsets,

@@ -1,10 +1,9 @@
-// Batch-1 decode path of the MoE layer: matrix-vector work that barely reuses
-// a weight, bound by memory bandwidth and run on the vector ALUs ("Decode
-// generates one token at a time ... GEMV work: memory-bandwidth-bound, and
-// better served by the GPU's regular vector ALUs": Lily page, section "Why
-// Apple Silicon isn't just a smaller datacenter GPU"), with kernel chains fused
-// so intermediates stay on chip (Inside Lily page, section "Performance Gains
-// and Workload Patterns").
+// Batch-1 decode path of the MoE layer.  With one token per step every weight
+// is used once, so the work is matrix-vector, limited by memory bandwidth, and
+// the pages assign it to the vector ALUs rather than the matrix units (Lily
+// page, section "Why Apple Silicon isn't just a smaller datacenter GPU"); chains
+// of kernels are fused so that intermediates stay on chip (Inside Lily page,
+// section "Performance Gains and Workload Patterns").
 //
 // Three launches per layer:
 //   1. router GEMV (fp32 weights)                      -> logits, shared-gate logit

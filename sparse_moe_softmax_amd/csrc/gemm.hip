@@ -92,62 +92,6 @@ struct GemmArgs {
   int T, k, H;
 };
 
-// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding).
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Direct global -> LDS loads through buffer instructions.  Lane i of the wave
-// writes its bytes at lds + i * 16 (16-byte form) or lds + i * 4 (4-byte form);
-// the source is the resource's base + a per-lane offset + a wave-uniform offset,
-// so that advancing a stream by one K block is a scalar add.  Issued through
-// inline asm so that the compiler does not add its own conservative vmcnt(0)
-// wait before every later LDS read: the K loop waits for exactly the stage it
-// consumes (wait_vmcnt) and then barriers.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-// Raw buffer resource at `base` covering the whole 32-bit offset range
-// (num_records all ones: no range clamp; offsets are in bytes).
-__device__ inline i32x4 buffer_rsrc(const void* base) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a));
-  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a >> 32));  // stride 0
-  r.z = -1;
-  r.w = 0x00020000;
-  return r;
-}
-__device__ inline uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-__device__ inline void bdma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
-}
-__device__ inline void bdma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-               : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
-}
-// vmcnt(n * per) for a runtime n in [0, MAXN] (s_waitcnt takes an immediate).
-template <int PER, int MAXN>
-__device__ inline void wait_stages(int n) {
-  if constexpr (MAXN > 0) {
-    if (n >= MAXN) {
-      wait_vmcnt<MAXN * PER>();
-      return;
-    }
-    wait_stages<PER, MAXN - 1>(n);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
-// Physical 16-byte chunk of logical chunk c in row r of an A stage.  The XOR
-// key (r ^ (r >> 3)) & 7 makes the 16-byte reads of any 8 consecutive rows, and
-// of the even and of the odd rows among any 16 consecutive rows, hit distinct
-// bank groups (conflict-free for 32- and 64-bank LDS).
-__device__ inline int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 // Stored position of 16-byte half h of weight row i in a B stage (row = 32 B):
 // rows are spread so that 8 (or 16) consecutive rows read distinct bank groups.
 // Applied once by the packing, so the stage is a plain copy of a packed block.

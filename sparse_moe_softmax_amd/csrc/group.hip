@@ -1,11 +1,11 @@
 // GPU-resident grouping of routed slots by expert: histogram, prefix-sum
-// offsets, stable permutation and tile block map, with no host round trip
-// ("Routing histograms and block maps remain inside GPU command buffers,
-// preventing costly CPU-to-GPU synchronization": Inside Lily page, section
-// "Performance Gains and Workload Patterns").
+// offsets, stable permutation and tile block map, with no host round trip.
+// The pages keep the routing histograms and block maps on the GPU so that no
+// CPU-GPU synchronisation is needed between routing and the expert GEMMs
+// (Inside Lily page, section "Performance Gains and Workload Patterns").
 //
 // Three steps, all on the device:
-//   1. per routing tile (64 tokens): expert histogram          (k_tile_hist, or fused into k_topk)
+//   1. per routing tile (kTopkTile tokens): expert histogram          (k_tile_hist, or fused into k_topk)
 //   2. per expert: exclusive scan of its count over the tiles  (k_group_scan, one block per expert)
 //   3. per tile: stable in-tile ranks from wavefront ballots,
 //      positions = offsets[e] + tile base + rank               (k_group_scatter)

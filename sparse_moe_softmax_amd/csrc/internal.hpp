@@ -28,7 +28,7 @@ constexpr int kWave = 64;
 #endif
 constexpr int kBM = MOE_BM;
 static_assert(kBM % 32 == 0, "tile height: whole 32-row MFMA sub-tiles");
-constexpr int kTopkTile = 64;       // tokens per routing tile (histogram granularity)
+constexpr int kTopkTile = 16;       // tokens per routing tile (histogram granularity)
 
 // ------------------------------------------------------------------ scalar helpers
 
@@ -98,6 +98,64 @@ __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------------ direct-to-LDS loads
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct global -> LDS loads through buffer instructions.  Lane i of the wave
+// writes its bytes at lds + i * 16 (16-byte form) or lds + i * 4 (4-byte form);
+// the source is the resource's base + a per-lane offset + a wave-uniform offset,
+// so that advancing a stream by one K block is a scalar add.  Issued through
+// inline asm so that the compiler does not add its own conservative vmcnt(0)
+// wait before every later LDS read: the K loop waits for exactly the stage it
+// consumes (wait_vmcnt) and then barriers.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// Raw buffer resource at `base` covering the whole 32-bit offset range
+// (num_records all ones: no range clamp; offsets are in bytes).
+__device__ inline i32x4 buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a >> 32));  // stride 0
+  r.z = -1;
+  r.w = 0x00020000;
+  return r;
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ inline void bdma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ inline void bdma4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+// vmcnt(n * per) for a runtime n in [0, MAXN] (s_waitcnt takes an immediate).
+template <int PER, int MAXN>
+__device__ inline void wait_stages(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * PER>();
+      return;
+    }
+    wait_stages<PER, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// Physical 16-byte chunk of logical chunk c in row r of an A stage.  The XOR
+// key (r ^ (r >> 3)) & 7 makes the 16-byte reads of any 8 consecutive rows, and
+// of the even and of the odd rows among any 16 consecutive rows, hit distinct
+// bank groups (conflict-free for 32- and 64-bank LDS).
+__device__ inline int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 // ------------------------------------------------------------------ top-k (device helpers)
 
 // Top-k of one token's E logits by a group of 16 lanes.  Lane j holds the
@@ -105,12 +163,11 @@ __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& 
 // lane's best unselected logit and reduces over the group with the order
 // "larger logit first, then lower expert index".  Results are identical in
 // all 16 lanes: top_e[r], top_v[r] for r < k.
-__device__ inline void topk16(const float* __restrict__ row, int E, int k, int j, int (&top_e)[16],
-                              float (&top_v)[16]) {
-  float v[16];
-  const int nper = E >> 4;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = (i < nper) ? row[i * 16 + j] : 0.f;
+// CONTIG == false: lane j holds experts j, j+16, j+32, ... (v[i] = expert 16i + j);
+// CONTIG == true:  lane j holds experts nper*j .. nper*j + nper - 1 (v[i] = expert nper*j + i).
+template <bool CONTIG = false>
+__device__ inline void topk16_regs(const float (&v)[16], int nper, int k, int j, int (&top_e)[16],
+                                   float (&top_v)[16]) {
   uint32_t sel = 0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -122,7 +179,7 @@ __device__ inline void topk16(const float* __restrict__ row, int E, int k, int j
         // ascending i = ascending expert id inside a lane: strict '>' keeps the lower id on ties
         if (i < nper && !((sel >> i) & 1u) && (be == 0x7FFFFFFF || v[i] > bv)) {
           bv = v[i];
-          be = i * 16 + j;
+          be = CONTIG ? nper * j + i : i * 16 + j;
         }
       }
 #pragma unroll
@@ -133,11 +190,24 @@ __device__ inline void topk16(const float* __restrict__ row, int E, int k, int j
         bv = take ? ov : bv;
         be = take ? oe : be;
       }
-      if ((be & 15) == j) sel |= 1u << (be >> 4);
+      if (CONTIG) {
+        const int ri = be - nper * j;          // slot of the winner if this lane owns it
+        if (ri >= 0 && ri < nper) sel |= 1u << ri;
+      } else if ((be & 15) == j) {
+        sel |= 1u << (be >> 4);
+      }
       top_e[r] = be;
       top_v[r] = bv;
     }
   }
+}
+__device__ inline void topk16(const float* __restrict__ row, int E, int k, int j, int (&top_e)[16],
+                              float (&top_v)[16]) {
+  float v[16];
+  const int nper = E >> 4;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = (i < nper) ? row[i * 16 + j] : 0.f;
+  topk16_regs(v, nper, k, j, top_e, top_v);
 }
 
 // Renormalised weights of the k kept experts: exp(l_r - l_0) / sum_r' exp(l_r' - l_0),
@@ -201,12 +271,21 @@ inline PackGeom pack_geom(const moe_dims& d, int matrix) {
 hipError_t launch_prepack_q4(const moe_dims& d, int matrix, const moe_q4& w, int n_exp, uint8_t* packed,
                              hipStream_t s);
 hipError_t launch_prepack_router(const float* w, uint16_t* w3, int E, int H, hipStream_t s);
+// Router GEMM with K split over `splits` workgroups (splits divides H/64).
+// splits == 1: out = logits (+ bias), s_out = shared logit (NULL to skip).
+// splits > 1: out = partial sums [splits][T][E], s_out = [splits][T], no bias.
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w3, const float* bias, const float* wsg, int T,
-                              int H, int E, float* logits, float* s_logit, float* y_zero, hipStream_t s);
+                              int H, int E, int splits, float* out, float* s_out, hipStream_t s);
+// K splits the fused layer uses for T tokens (enough workgroups to fill the chip).
+int router_splits(int T, int H, int E);
 hipError_t launch_router_gemv(const uint16_t* x, const float* w, const float* bias, const float* wsg, int T, int H,
                               int E, float* logits, float* s_logit, hipStream_t s);
-hipError_t launch_topk(const float* logits, const float* s_logit, int T, int E, int k, int32_t* ids, float* wts,
-                       float* gate, int32_t* tilehist, hipStream_t s);
+// Top-k from router output: splits == 1 reads final logits (and shared logit);
+// splits > 1 sums the partials in split order, adds the bias and writes the
+// final logits / shared logit to logits_out / s_out when given.
+hipError_t launch_topk(const float* parts, const float* s_parts, int splits, const float* bias, int T, int E, int k,
+                       float* logits_out, float* s_out, int32_t* ids, float* wts, float* gate, int32_t* tilehist,
+                       hipStream_t s);
 hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, hipStream_t s);
 hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
                         int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,

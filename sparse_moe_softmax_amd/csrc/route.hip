@@ -1,8 +1,8 @@
 // Router: logits = x . W_r^T (+ bias), shared-gate logit, top-k selection with
 // renormalised softmax weights, and the per-tile expert histogram that the
-// grouping step scans.  ("A router scores 256 expert subnetworks and picks 8,
-// plus a shared expert that runs on every token regardless": Lily page,
-// section "The architecture that forces the issue: MoE plus Gated DeltaNet".)
+// grouping step scans.  Each token is scored against all 256 routed experts,
+// the best 8 are kept, and the shared expert runs for every token (Lily page,
+// section "The architecture that forces the issue: MoE plus Gated DeltaNet").
 #include "internal.hpp"
 
 namespace moe {
@@ -32,105 +32,158 @@ hipError_t launch_prepack_router(const float* w, uint16_t* w3, int E, int H, hip
 
 // ------------------------------------------------------------------ router GEMM (T > 1)
 
-// Tile of 64 tokens x 64 experts, K in blocks of 64.  Wave w owns experts
-// [e0 + 16w, e0 + 16w + 16) for all 64 tokens (4 MFMA row sub-tiles).  The
-// bf16 x tile is staged in LDS; the three weight planes come straight from
-// global memory as MFMA B fragments.  Within a 64-wide K block the lane
-// group q = lane/16 covers K offsets [16q, 16q+16): fragment s of a lane holds
-// offsets 16q + 8s .. 16q + 8s + 7 for both operands (a consistent
-// permutation of K, which leaves the dot products unchanged).
+// Tile of 64 tokens x 64 experts over one K range (K may be split over
+// gridDim.z workgroups so that small T still fills the chip).  Per 64-wide K
+// block, direct-to-LDS loads bring the bf16 x tile (8 KB), the three bf16
+// weight planes of the 64 experts (24 KB) and the 64 shared-gate weights into
+// a ring of kRtStages stages, refilled kRtStages-1 blocks ahead (the same
+// explicit-vmcnt scheme as the grouped GEMM; rows XOR-swizzled by a_chunk).
+// Wave w owns experts [16w, 16w + 16) of the tile for all 64 tokens (4 MFMA
+// row sub-tiles of v_mfma_f32_16x16x32_bf16).  Within a K block the lane group
+// q = lane/16 covers K offsets [16q, 16q+16): k-step s of a lane holds offsets
+// 16q + 8s .. +7 for both operands (a consistent permutation of K).
+// Workgroups of the first expert tile also form the shared-gate dot product
+// on the vector ALUs from the staged x tile.
+// One split: logits (+ bias) and s_logit are final.  Several: partial sums
+// part[z][T][E], s_part[z][T] without bias, summed in z order by k_topk.
 constexpr int kRtM = 64;
 constexpr int kRtN = 64;
-constexpr int kLdA = 64 + 8;  // padded LDS row (144 B) to spread banks
+constexpr int kRtStages = 4;
+constexpr int kRtX = kRtM * 128;                  // x tile
+constexpr int kRtW = 3 * kRtN * 128;              // weight planes
+constexpr int kRtS = 4 * 256;                     // shared-gate weights (one copy per wave)
+constexpr int kRtStage = kRtX + kRtW + kRtS;
+constexpr int kRtDma = 2 + 6 + 1;                 // loads per wave per stage
+constexpr int kMaxSplits = 8;                     // K splits at most
 
 __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w3,
                                                      const float* __restrict__ bias, const float* __restrict__ wsg,
-                                                     int T, int H, int E, float* __restrict__ logits,
-                                                     float* __restrict__ s_logit, float* __restrict__ y_zero) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kRtM * kLdA];
+                                                     int T, int H, int E, int kbs, float* __restrict__ out,
+                                                     float* __restrict__ s_out) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRtStages * kRtStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int col = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * kRtM;
   const int rows = min(kRtM, T - t0);
-  const int e_w = blockIdx.y * kRtN + wave * 16;
-  const bool active = e_w < E;
-  const int col = lane & 15;
-  const int q = lane >> 4;
-  const bool do_s = (blockIdx.y == 0) && (s_logit != nullptr);
+  const int e0 = blockIdx.y * kRtN;
+  const int z = blockIdx.z;
+  const int splits = gridDim.z;
+  const int kb0 = z * kbs;
+  const bool do_s = blockIdx.y == 0 && s_out != nullptr;
 
-  // zero this block's share of the fp32 combine buffer (moe_forward only)
-  if (y_zero) {
-    const int ny = gridDim.y;
-    const int cw = static_cast<int>(div_up(div_up(H, ny), 4) * 4);
-    const int c0 = blockIdx.y * cw;
-    const int c1 = min(H, c0 + cw);
-    const int w4 = (c1 - c0) / 4;
-    for (int i = tid; i < rows * w4; i += 256) {
-      const int r = i / w4, c = c0 + 4 * (i % w4);
-      *reinterpret_cast<float4*>(y_zero + static_cast<int64_t>(t0 + r) * H + c) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+  // per-lane load offsets (bytes); rows past T or E re-read the last valid row
+  uint32_t xoff[2], woff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (wave * 2 + j) * 8 + (lane >> 3);
+    const int p = lane & 7;
+    int c = 0;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+      if (a_chunk(r, cc) == p) c = cc;
+    xoff[j] = (static_cast<uint32_t>(t0 + min(r, rows - 1)) * H + kb0 * 64 + c * 8) * 2;
+    woff[j] = (static_cast<uint32_t>(min(e0 + r, E - 1)) * H + kb0 * 64 + c * 8) * 2;
   }
+  const uint32_t plane_bytes = static_cast<uint32_t>(E) * H * 2;
+  const i32x4 xr = buffer_rsrc(x), wr = buffer_rsrc(w3), sr = buffer_rsrc(wsg);
+  const uint32_t soff = (kb0 * 64 + lane) * 4;
+  const uint32_t ring_s = lds_addr(ring);
+
+  auto issue = [&](int kb) {
+    const uint32_t st = ring_s + (kb % kRtStages) * kRtStage;
+    const uint32_t ko = kb * 128;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bdma16(xr, xoff[j], ko, st + (wave_s * 2 + j) * 1024);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bdma16(wr, woff[j] + p * plane_bytes, ko, st + kRtX + p * 8192 + (wave_s * 2 + j) * 1024);
+    bdma4(sr, soff, kb * 256, st + kRtX + kRtW + wave_s * 256);
+  };
 
   f32x4 acc[4];
+#pragma unroll
   for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   float s_acc = 0.f;
   const int s_tok = tid >> 2, s_q = tid & 3;
-  const int64_t plane = static_cast<int64_t>(E) * H;
-  const uint16_t* wrow = w3 + static_cast<int64_t>(active ? e_w + col : 0) * H;
 
-  for (int kb = 0; kb < H / 64; ++kb) {
-    // stage x[t0 .. t0+63][kb*64 .. +63] into LDS: 512 chunks of 16 B
-    for (int c = tid; c < kRtM * 8; c += 256) {
-      const int r = c >> 3, c8 = c & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < rows) v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t0 + r) * H + kb * 64 + c8 * 8);
-      *reinterpret_cast<uint4*>(As + r * kLdA + c8 * 8) = v;
-    }
-    __syncthreads();
-    if (active) {
-      // planes in order lo, mid, hi
-      for (int p = 2; p >= 0; --p) {
-        const uint16_t* src = wrow + p * plane + kb * 64 + q * 16;
-        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(src);
-        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(src + 8);
-        for (int m = 0; m < 4; ++m) {
-          const uint16_t* ap = As + (m * 16 + col) * kLdA + q * 16;
-          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap);
-          const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + 8);
-          acc[m] = mfma16(a0, b0, acc[m]);
-          acc[m] = mfma16(a1, b1, acc[m]);
-        }
+#pragma unroll
+  for (int st = 0; st < kRtStages - 1; ++st)
+    if (st < kbs) issue(st);
+  for (int kb = 0; kb < kbs; ++kb) {
+    // issued so far: stages 0 .. min(kb + kRtStages - 2, kbs - 1); wait for stage kb
+    wait_stages<kRtDma, kRtStages - 2>(min(kRtStages - 2, kbs - 1 - kb));
+    __builtin_amdgcn_s_barrier();  // stage kb landed for every wave; stage kb-1 consumed
+    if (kb + kRtStages - 1 < kbs) issue(kb + kRtStages - 1);
+    const unsigned char* st = ring + (kb % kRtStages) * kRtStage;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 a[4], b[3];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = m * 16 + col;
+        a[m] = *reinterpret_cast<const bf16x8*>(st + r * 128 + (a_chunk(r, 2 * q + ks) << 4));
       }
+      const int er = wave * 16 + col;
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        b[p] = *reinterpret_cast<const bf16x8*>(st + kRtX + p * 8192 + er * 128 + (a_chunk(er, 2 * q + ks) << 4));
+#pragma unroll
+      for (int p = 2; p >= 0; --p)   // planes lo, mid, hi
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = mfma16(a[m], b[p], acc[m]);
     }
     if (do_s) {
-      const uint16_t* ap = As + s_tok * kLdA + s_q * 16;
-      const float* wp = wsg + kb * 64 + s_q * 16;
-      for (int i = 0; i < 16; ++i) s_acc = __builtin_fmaf(bf16_to_f32(ap[i]), wp[i], s_acc);
-    }
-    __syncthreads();
-  }
-
-  if (active) {
-    const float b = bias ? bias[e_w + col] : 0.f;
-    for (int m = 0; m < 4; ++m) {
-      for (int i = 0; i < 4; ++i) {
-        const int r = m * 16 + q * 4 + i;
-        if (r < rows) logits[static_cast<int64_t>(t0 + r) * E + e_w + col] = acc[m][i] + b;
+      const float* wsl = reinterpret_cast<const float*>(st + kRtX + kRtW);   // wave 0's copy
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * s_q + h;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + s_tok * 128 + (a_chunk(s_tok, c) << 4));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_acc = __builtin_fmaf(static_cast<float>(v[i]), wsl[c * 8 + i], s_acc);
       }
     }
+  }
+
+  const int e = e0 + wave * 16 + col;
+  if (e < E) {
+    const bool last = splits == 1;
+    const float b = (last && bias) ? bias[e] : 0.f;
+    float* o = out + static_cast<int64_t>(z) * T * E;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m * 16 + q * 4 + i;
+        if (r < rows) o[static_cast<int64_t>(t0 + r) * E + e] = acc[m][i] + b;
+      }
   }
   if (do_s) {
     s_acc += __shfl_xor(s_acc, 1);
     s_acc += __shfl_xor(s_acc, 2);
-    if (s_q == 0 && s_tok < rows) s_logit[t0 + s_tok] = s_acc;
+    if (s_q == 0 && s_tok < rows) s_out[static_cast<int64_t>(z) * T + t0 + s_tok] = s_acc;
   }
 }
 
+int router_splits(int T, int H, int E) {
+  const int64_t tiles = div_up(T, kRtM) * div_up(E, kRtN);
+  const int kg = H / 64;
+  int want = static_cast<int>(div_up(256, tiles));
+  want = want < 1 ? 1 : (want > kMaxSplits ? kMaxSplits : want);
+  while (want > 1 && kg % want) --want;
+  return want;
+}
+
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w3, const float* bias, const float* wsg, int T,
-                              int H, int E, float* logits, float* s_logit, float* y_zero, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(div_up(T, kRtM)), static_cast<unsigned>(div_up(E, kRtN)));
-  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, w3, bias, wsg, T, H, E, logits, s_logit, y_zero);
+                              int H, int E, int splits, float* out, float* s_out, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(div_up(T, kRtM)), static_cast<unsigned>(div_up(E, kRtN)),
+            static_cast<unsigned>(splits));
+  const float* wsg_src = wsg ? wsg : reinterpret_cast<const float*>(w3);   // loaded but unused without s_out
+  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, w3, bias, wsg_src, T, H, E, H / 64 / splits, out,
+                     wsg ? s_out : nullptr);
   return hipGetLastError();
 }
 
@@ -176,12 +229,18 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* w, const float* bi
 
 // ------------------------------------------------------------------ top-k
 
-// One block = one routing tile of 64 tokens; 16 groups of 16 lanes take 16
-// tokens at a time.  Optionally counts the tile's expert histogram.
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ s_logit,
-                                              int T, int E, int k, int32_t* __restrict__ ids,
-                                              float* __restrict__ wts, float* __restrict__ gate,
-                                              int32_t* __restrict__ tilehist) {
+// One block = one routing tile of kTopkTile tokens, one group of 16 lanes per
+// token; lane j holds experts [16j, 16j + 16) (E / 16 of them), loaded as float4.
+// With several router splits the logits are first summed over the splits in
+// order (plus the bias) and written out.  Optionally counts the tile's expert
+// histogram.
+static_assert(kTopkTile * 16 == 256, "one 256-thread block per routing tile");
+
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ parts, const float* __restrict__ s_parts,
+                                              int splits, const float* __restrict__ bias, int T, int E, int k,
+                                              float* __restrict__ logits_out, float* __restrict__ s_out,
+                                              int32_t* __restrict__ ids, float* __restrict__ wts,
+                                              float* __restrict__ gate, int32_t* __restrict__ tilehist) {
   __shared__ int hist[256];
   const int tid = threadIdx.x;
   const int grp = tid >> 4, j = tid & 15;
@@ -189,22 +248,79 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     for (int e = tid; e < E; e += 256) hist[e] = 0;
     __syncthreads();
   }
-  for (int it = 0; it < kTopkTile / 16; ++it) {
-    const int t = blockIdx.x * kTopkTile + it * 16 + grp;
-    if (t < T) {
-      int te[16];
-      float tv[16], w[16];
-      topk16(logits + static_cast<int64_t>(t) * E, E, k, j, te, tv);
-      topk_weights(k, tv, w);
+  const int t = blockIdx.x * kTopkTile + grp;
+  if (t < T) {
+    const int nper = E >> 4;        // 1..16, a multiple of 4 when E % 64 == 0
+    const int64_t TE = static_cast<int64_t>(T) * E;
+    const int64_t o = static_cast<int64_t>(t) * E + nper * j;
+    float v[16];
+    if ((nper & 3) == 0) {
+      float4 p[kMaxSplits][4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (r < k && r == j) {
-          ids[static_cast<int64_t>(t) * k + r] = te[r];
-          wts[static_cast<int64_t>(t) * k + r] = w[r];
-          if (tilehist) atomicAdd(&hist[te[r]], 1);
+      for (int zz = 0; zz < kMaxSplits; ++zz)
+        if (zz < splits)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (4 * c < nper) p[zz][c] = *reinterpret_cast<const float4*>(parts + zz * TE + o + 4 * c);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (4 * c < nper) {
+          float4 l = p[0][c];
+#pragma unroll
+          for (int zz = 1; zz < kMaxSplits; ++zz)
+            if (zz < splits) {
+              l.x += p[zz][c].x;
+              l.y += p[zz][c].y;
+              l.z += p[zz][c].z;
+              l.w += p[zz][c].w;
+            }
+          v[4 * c] = l.x;
+          v[4 * c + 1] = l.y;
+          v[4 * c + 2] = l.z;
+          v[4 * c + 3] = l.w;
         }
       }
-      if (gate && s_logit && j == 0) gate[t] = sigmoidf_(s_logit[t]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < nper) {
+          float l = parts[o + i];
+          for (int zz = 1; zz < splits; ++zz) l += parts[zz * TE + o + i];
+          v[i] = l;
+        }
+      }
+    }
+    if (splits > 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < nper) {
+          if (bias) v[i] += bias[nper * j + i];
+          if (logits_out) logits_out[o + i] = v[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i >= nper) v[i] = 0.f;
+    int te[16];
+    float tv[16], w[16];
+    topk16_regs<true>(v, nper, k, j, te, tv);
+    topk_weights(k, tv, w);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r < k && r == j) {
+        ids[static_cast<int64_t>(t) * k + r] = te[r];
+        wts[static_cast<int64_t>(t) * k + r] = w[r];
+        if (tilehist) atomicAdd(&hist[te[r]], 1);
+      }
+    }
+    if (s_parts && j == 0) {
+      float sl = s_parts[t];
+      if (splits > 1) {
+        for (int zz = 1; zz < splits; ++zz) sl += s_parts[static_cast<int64_t>(zz) * T + t];
+        if (s_out) s_out[t] = sl;
+      }
+      if (gate) gate[t] = sigmoidf_(sl);
     }
   }
   if (tilehist) {
@@ -213,10 +329,11 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   }
 }
 
-hipError_t launch_topk(const float* logits, const float* s_logit, int T, int E, int k, int32_t* ids, float* wts,
-                       float* gate, int32_t* tilehist, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(static_cast<unsigned>(div_up(T, kTopkTile))), dim3(256), 0, s, logits, s_logit, T,
-                     E, k, ids, wts, gate, tilehist);
+hipError_t launch_topk(const float* parts, const float* s_parts, int splits, const float* bias, int T, int E, int k,
+                       float* logits_out, float* s_out, int32_t* ids, float* wts, float* gate, int32_t* tilehist,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3(static_cast<unsigned>(div_up(T, kTopkTile))), dim3(256), 0, s, parts, s_parts,
+                     splits, bias, T, E, k, logits_out, s_out, ids, wts, gate, tilehist);
   return hipGetLastError();
 }
 
