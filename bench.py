@@ -101,7 +101,7 @@ def bench_prefill(cfg, steps, warmup):
     x_cpu = synth.activations(cfg.T, d.hidden, cfg.seed)
     x = x_cpu.cuda()
     T = cfg.T
-    ws = torch.empty(moe.moe_workspace_bytes(md, T), dtype=torch.uint8, device="cuda")
+    ws = moe.moe_workspace(md, T)
     y = torch.empty((T, d.hidden), dtype=torch.bfloat16, device="cuda")
     logits = torch.empty((T, d.n_experts), dtype=torch.float32, device="cuda")
     ids = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
@@ -141,7 +141,7 @@ def bench_decode(cfg, n_steps, graph_chunk=32):
         lay = synth.make_layer(d, cfg.seed, layer=l, device="cuda")
         layers.append(device_layer(lay, d, moe))
     xs = torch.stack([synth.activations(1, d.hidden, cfg.seed, step=s)[0] for s in range(n_steps)]).cuda()
-    ws = torch.empty(moe.moe_workspace_bytes(md, 1), dtype=torch.uint8, device="cuda")
+    ws = moe.moe_workspace(md, 1)
     ys = torch.empty((cfg.layers, d.hidden), dtype=torch.bfloat16, device="cuda")
 
     def step(s):

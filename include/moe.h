@@ -196,13 +196,19 @@ moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue 
                                const int32_t* n_tiles, int32_t max_tiles, const float* row_weight, int32_t T,
                                int32_t block_m, void* out, void* stream);
 
-/* Scratch bytes moe_forward() needs for up to T_max tokens. */
+/* Scratch bytes moe_forward() needs for up to T_max tokens.  The first 256
+ * bytes hold the synchronisation counters of the T == 1 path: they must be
+ * zero before a workspace's first T == 1 call (allocate it zero-filled), and
+ * every call leaves them zero. */
 size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
 
 /* The whole layer for T tokens:
  *   y[t] = bf16( sum_j w[t][j] * E_{ids[t][j]}(x[t]) + g[t] * E_shared(x[t]) ),
  *   E(x) = ( silu(x.Wg^T) * (x.Wu^T) ) . Wd^T with the SwiGLU product rounded to bf16.
- * T == 1 runs the decode path (vector-ALU GEMV, fp32 router_w); T > 1 runs
+ * T == 1 runs the decode path: one launch for the whole layer (vector-ALU
+ * GEMV on the canonical weights, fp32 router_w), whose workgroups hand results
+ * to each other through counters in the workspace (see moe_workspace_bytes;
+ * needs hidden <= 4096, inter and shared_inter <= 1024); T > 1 runs
  * router GEMM, top-k, grouping, the two grouped GEMMs on the matrix cores
  * (needs router_w3 and the packed weights of all four matrices) and the combine: the down GEMM stores every slot's
  * weighted output in fp16 and a final pass sums each token's k+1 entries in
@@ -214,12 +220,11 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t
                        float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
-/* The stages of moe_forward, in order.  T > 1: router GEMM (also zeroes the
- * fp32 combine buffer), top-k + tile histogram, grouping, gate/up grouped GEMM
+/* The stages of moe_forward, in order.  T > 1: router GEMM (partial sums over
+ * K splits when T is small), top-k + tile histogram, grouping, gate/up grouped GEMM
  * (+ shared expert), down grouped GEMM writing the weighted slot outputs
- * (+ shared expert), combine to bf16.  T == 1: ROUTER = router GEMV,
- * GATE_UP = top-k + gate/up GEMV + SwiGLU, DOWN = down GEMV + combine + bf16;
- * the other stages are empty. */
+ * (+ shared expert), combine to bf16.  T == 1: the fused layer runs as the
+ * ROUTER stage; the other stages are empty. */
 typedef enum moe_stage {
   MOE_STAGE_ROUTER = 0,
   MOE_STAGE_TOPK = 1,

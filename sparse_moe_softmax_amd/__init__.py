@@ -18,7 +18,8 @@ import torch  # first: libmoe then binds to the HIP runtime torch already loaded
 __all__ = [
     "Dims", "MoeError", "LayerWeights", "lib", "moe_block_m", "moe_max_tiles", "moe_prepack_router",
     "moe_router_logits", "moe_route", "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4",
-    "moe_workspace_bytes", "moe_forward", "moe_forward_stages", "moe_packed_q4_bytes", "moe_prepack_q4",
+    "moe_workspace_bytes", "moe_workspace", "moe_forward", "moe_forward_stages", "moe_packed_q4_bytes",
+    "moe_prepack_q4",
     "MOE_EPI_SWIGLU_BF16",
     "MOE_EPI_WEIGHTED_SCATTER_F32", "STAGES",
     "EXPORTED_SYMBOLS",
@@ -261,13 +262,19 @@ def moe_workspace_bytes(d, T_max: int) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(_dims(d)), T_max))
 
 
+def moe_workspace(d, T_max: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for moe_forward with up to T_max tokens (the
+    T == 1 path keeps counters in it that must start at zero)."""
+    return torch.zeros((moe_workspace_bytes(d, T_max),), dtype=torch.uint8, device=device)
+
+
 def moe_forward(d, layer: LayerWeights, x: torch.Tensor, y=None, logits_out=None, ids_out=None, w_out=None,
                 workspace: torch.Tensor | None = None) -> torch.Tensor:
     T = x.shape[0]
     if y is None:
         y = _empty((T, d.hidden), torch.bfloat16, x)
     if workspace is None:
-        workspace = _empty((moe_workspace_bytes(d, T),), torch.uint8, x)
+        workspace = moe_workspace(d, T, x.device)
     _check(lib().moe_forward(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y), _ptr(logits_out),
                              _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(), _stream()))
     return y

@@ -72,8 +72,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 // Workspace regions of moe_forward.
 struct Ws {
-  size_t logits, s, rparts, sparts, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh,
-      slots, hdec;
+  size_t sync, logits, s, rparts, sparts, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh,
+      slots;
   int splits;
   size_t total;
 };
@@ -83,7 +83,6 @@ Ws layout(const moe_dims& d, int32_t T) {
   const size_t F = static_cast<size_t>(T) * k;
   const size_t ntile = static_cast<size_t>(div_up(T, kTopkTile));
   const size_t mt = static_cast<size_t>(moe_max_tiles(T, d.top_k, d.n_experts, kBM));
-  const size_t ldh = static_cast<size_t>(div_up(std::max(I, Is), 8) * 8);
   Ws w{};
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -91,6 +90,7 @@ Ws layout(const moe_dims& d, int32_t T) {
     o = align256(o + bytes);
     return at;
   };
+  w.sync = take(decode_sync_bytes(d));   // T == 1 hand-over words: first, never written by the T > 1 path
   w.logits = take(T * E * 4);
   w.s = take(T * 4);
   w.splits = T > 1 ? router_splits(T, d.hidden, d.n_experts) : 1;
@@ -110,7 +110,6 @@ Ws layout(const moe_dims& d, int32_t T) {
   w.h = take(F * I * 2);
   w.hsh = take(static_cast<size_t>(T) * Is * 2);
   w.slots = take(static_cast<size_t>(T) * (k + 1) * H * 2);
-  w.hdec = take((k + 1) * ldh * 2);
   w.total = o;
   return w;
 }
@@ -291,6 +290,8 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   if (!workspace || workspace_bytes < w.total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, w.total);
   if (T == 1 && !L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+  if (T == 1 && !decode_supported(*d))
+    return fail(MOE_ERR_UNSUPPORTED, "T == 1 needs hidden <= 4096, inter and shared_inter <= 1024");
   if (T > 1 && !L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
   if (T > 1 && (st = check_gemm_extent(*d, T))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -302,9 +303,9 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   auto run = [&](int stage) { return first <= stage && stage <= last; };
 
   if (T == 1) {
-    DecodePtrs p{logits, s_logit, ids, wts, gate, at<uint16_t>(workspace, w.hdec)};
-    for (int stage = first; stage <= last; ++stage)
-      if ((st = hip_check(launch_decode_stage(*d, *L, x, y, p, stage, s), "decode"))) return st;
+    // one fused launch for the whole layer, run as the ROUTER stage
+    DecodePtrs p{logits, s_logit, ids, wts, gate, at<void>(workspace, w.sync)};
+    if (run(MOE_STAGE_ROUTER)) return hip_check(launch_decode_layer(*d, *L, x, y, p, s), "decode layer");
     return MOE_OK;
   }
   uint16_t* slots = at<uint16_t>(workspace, w.slots);

@@ -163,44 +163,101 @@ __device__ inline int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 // lane's best unselected logit and reduces over the group with the order
 // "larger logit first, then lower expert index".  Results are identical in
 // all 16 lanes: top_e[r], top_v[r] for r < k.
+// Top-k keys: the order "larger logit first, then lower expert index" as one
+// unsigned 64-bit comparison.  High half: the logit's bits mapped so that
+// unsigned order is float order (-0 folded into +0, so that they tie); low
+// half: ~expert.  Every key of a finite logit is > 0, so 0 means "none".
+__device__ inline uint64_t topk_key(float v, int e) {
+  uint32_t b = __float_as_uint(v + 0.0f);          // -0 + +0 = +0
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(b) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+}
+__device__ inline float topk_key_value(uint64_t key) {
+  const uint32_t b = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
+}
+__device__ inline int topk_key_expert(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+// max(key, key of the partner lane under a DPP row permutation)
+template <int CTRL>
+__device__ inline uint64_t dpp_max(uint64_t key) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<uint32_t>(key), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, static_cast<uint32_t>(key >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > key ? o : key;
+}
+// max over a 16-lane DPP row (lane ^ 1, lane ^ 2, mirror within 8, mirror
+// within 16: afterwards every lane of the row holds the row maximum)
+__device__ inline uint64_t row_max16(uint64_t key) {
+  key = dpp_max<0xB1>(key);    // quad_perm [1,0,3,2]
+  key = dpp_max<0x4E>(key);    // quad_perm [2,3,0,1]
+  key = dpp_max<0x141>(key);   // row_half_mirror
+  return dpp_max<0x140>(key);  // row_mirror
+}
+
+// Top-k of one token's logits by a group of 16 lanes that forms one DPP row
+// (lanes 16r .. 16r+15).  Each of the k rounds takes every lane's largest
+// remaining key, reduces over the row, and the lane that holds the winner
+// drops it (keys are unique).
 // CONTIG == false: lane j holds experts j, j+16, j+32, ... (v[i] = expert 16i + j);
 // CONTIG == true:  lane j holds experts nper*j .. nper*j + nper - 1 (v[i] = expert nper*j + i).
 template <bool CONTIG = false>
 __device__ inline void topk16_regs(const float (&v)[16], int nper, int k, int j, int (&top_e)[16],
                                    float (&top_v)[16]) {
-  uint32_t sel = 0;
+  uint64_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) key[i] = (i < nper) ? topk_key(v[i], CONTIG ? nper * j + i : i * 16 + j) : 0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r < k) {
-      float bv = 0.f;
-      int be = 0x7FFFFFFF;
+      uint64_t best = key[0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // ascending i = ascending expert id inside a lane: strict '>' keeps the lower id on ties
-        if (i < nper && !((sel >> i) & 1u) && (be == 0x7FFFFFFF || v[i] > bv)) {
-          bv = v[i];
-          be = CONTIG ? nper * j + i : i * 16 + j;
-        }
-      }
+      for (int i = 1; i < 16; ++i) best = key[i] > best ? key[i] : best;
+      best = row_max16(best);
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 16);
-        const int oe = __shfl_xor(be, off, 16);
-        const bool take = (oe != 0x7FFFFFFF) && (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
-        bv = take ? ov : bv;
-        be = take ? oe : be;
-      }
-      if (CONTIG) {
-        const int ri = be - nper * j;          // slot of the winner if this lane owns it
-        if (ri >= 0 && ri < nper) sel |= 1u << ri;
-      } else if ((be & 15) == j) {
-        sel |= 1u << (be >> 4);
-      }
-      top_e[r] = be;
-      top_v[r] = bv;
+      for (int i = 0; i < 16; ++i) key[i] = key[i] == best ? 0 : key[i];
+      top_e[r] = topk_key_expert(best);
+      top_v[r] = topk_key_value(best);
     }
   }
 }
+
+// Top-k of E <= 256 logits (in LDS) by one whole wave: lane l holds experts
+// l, l + 64, l + 128, l + 192.  Rounds as in topk16_regs, with the four row
+// maxima combined through readlane.  Results are the same in every lane.
+__device__ inline void topk_wave64(const float* __restrict__ logits, int E, int k, int (&top_e)[16],
+                                   float (&top_v)[16]) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? topk_key(logits[e], e) : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < k) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+      best = row_max16(best);
+      uint64_t w = best;
+#pragma unroll
+      for (int row = 0; row < 4; ++row) {
+        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(best), 16 * row);
+        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(best >> 32), 16 * row);
+        const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+        w = (row == 0 || o > w) ? o : w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[i] = key[i] == w ? 0 : key[i];
+      top_e[r] = topk_key_expert(w);
+      top_v[r] = topk_key_value(w);
+    }
+  }
+}
+
 __device__ inline void topk16(const float* __restrict__ row, int E, int k, int j, int (&top_e)[16],
                               float (&top_v)[16]) {
   float v[16];
@@ -307,11 +364,13 @@ struct DecodePtrs {
   int32_t* ids;
   float* wts;
   float* gate;
-  uint16_t* h;
+  void* sync;        // decode_sync_bytes(), zero before the first call on it
 };
-// One stage (MOE_STAGE_*) of the T == 1 path; stages without decode work are no-ops.
-hipError_t launch_decode_stage(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y,
-                               const DecodePtrs& p, int stage, hipStream_t s);
+// The whole T == 1 layer as one launch (router, top-k, experts, combine).
+hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y,
+                               const DecodePtrs& p, hipStream_t s);
+bool decode_supported(const moe_dims& d);
+size_t decode_sync_bytes(const moe_dims& d);
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -353,6 +353,29 @@ def test_decode_layers():
             gu.forward_and_check(c.dims, lay, x)
 
 
+def test_decode_handover_words():
+    """The fused T == 1 layer passes logits and h between its workgroups in
+    tagged words at the start of the workspace: after n calls every block has
+    recorded n completed calls, no wait timed out, and repeated calls on one
+    workspace give identical outputs."""
+    say("decode hand-over words")
+    m = gu.moe()
+    c = synth.CONFIGS["decode"]
+    md = gu.to_dims(c.dims)
+    dl = gu.device_layer(synth.make_layer(c.dims, c.seed, layer=3), c.dims)
+    ws = m.moe_workspace(md, 1)
+    outs = []
+    for step in range(6):
+        x = synth.activations(1, c.dims.hidden, c.seed, step=step % 2).cuda()
+        outs.append(m.moe_forward(md, dl, x, workspace=ws).clone())
+        torch.cuda.synchronize()
+        words = ws[:1028].view(torch.int32).cpu()
+        assert torch.all(words[:256] == step + 1)      # calls completed, per block
+        assert int(words[256]) == 0                     # timeout word
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[0], outs[4])
+    assert torch.equal(outs[1], outs[3]) and torch.equal(outs[1], outs[5])
+
+
 def test_forward_repeatable():
     say("forward repeatable")
     m = gu.moe()
@@ -383,7 +406,7 @@ def test_graph_capture_replays(T):
     dl = gu.device_layer(lay, d)
     md = gu.to_dims(d)
     x = synth.activations(T, d.hidden, 88 + T).cuda()
-    ws = torch.empty(m.moe_workspace_bytes(md, T), dtype=torch.uint8, device="cuda")
+    ws = m.moe_workspace(md, T)
     ids_e = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
     y_e = m.moe_forward(md, dl, x, ids_out=ids_e, workspace=ws).clone()
     ids_g = torch.empty_like(ids_e)
