@@ -61,32 +61,31 @@ def synth_dims_shared(d):
                       shared_inter=d.shared_inter)
 
 
-def device_layer(lay, d, moe):
+def device_layer(lay, d, moe, pack=True):
     import torch
     t = lambda a: None if a is None else a.to("cuda").contiguous()
     q = lambda m: tuple(t(a) for a in m)
     return moe.LayerWeights(moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter),
                             q(lay.gate_up), q(lay.down), q(lay.sh_gate_up), q(lay.sh_down), t(lay.router_w),
-                            t(lay.shared_gate_w), t(lay.router_bias))
+                            t(lay.shared_gate_w), t(lay.router_bias), pack=pack)
 
 
 def time_stages(moe, md, dl, x, y, ws, reps):
-    """Average GPU time (us) of each stage of the layer, HIP events on the launch stream."""
+    """Average GPU time (us) of each stage of the layer, measured inside whole
+    layers: HIP events recorded between the stages on the launch stream."""
     import torch
-    out = {}
-    for i, name in enumerate(moe.STAGES):
-        moe.moe_forward(md, dl, x, y=y, workspace=ws)        # refresh every stage's inputs
-        moe.moe_forward_stages(md, dl, x, y, ws, i, i)       # warm
-        s = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        for _ in range(reps):
-            moe.moe_forward_stages(md, dl, x, y, ws, i, i)
-        e1.record(s)
-        torch.cuda.synchronize()
-        out[name] = e0.elapsed_time(e1) * 1000.0 / reps
+    n = len(moe.STAGES)
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(reps)]
     moe.moe_forward(md, dl, x, y=y, workspace=ws)
-    return out
+    for r in range(reps):
+        for i in range(n):
+            ev[r][i].record(s)
+            moe.moe_forward_stages(md, dl, x, y, ws, i, i)
+        ev[r][n].record(s)
+    torch.cuda.synchronize()
+    return {name: sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) * 1000.0 / reps
+            for i, name in enumerate(moe.STAGES)}
 
 
 def bench_prefill(cfg, steps, warmup):
@@ -110,23 +109,38 @@ def bench_prefill(cfg, steps, warmup):
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
+    # eager launches (one host call per layer, seven kernels)
     e0.record(s)
     for _ in range(steps):
         moe.moe_forward(md, dl, x, y=y, workspace=ws)
     e1.record(s)
     torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+    # the timed steps: the layer captured once as a HIP graph and replayed
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(md, dl, x, y=y, workspace=ws)
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1000.0 / steps
     gpu_ms = e0.elapsed_time(e1) / steps
-    log(f"prefill {cfg.name}: {wall_ms:.4f} ms/step wall, {gpu_ms:.4f} ms/step gpu events")
+    log(f"prefill {cfg.name}: {wall_ms:.4f} ms/step wall, {gpu_ms:.4f} ms/step gpu events (HIP graph); "
+        f"eager launches {eager_ms:.4f} ms/step")
     stages = time_stages(moe, md, dl, x, y, ws, reps=max(10, steps))
     log("stages (us):", {k: round(v, 2) for k, v in stages.items()})
     # final forward with routing outputs kept for the cross-check in the CPU leg
     moe.moe_forward(md, dl, x, y=y, logits_out=logits, ids_out=ids, workspace=ws)
     torch.cuda.synchronize()
-    return {"cfg": cfg, "lay": lay, "x_cpu": x_cpu, "wall_ms": wall_ms, "gpu_ms": gpu_ms, "stages": stages,
-            "y": y, "logits": logits, "ids": ids}
+    return {"cfg": cfg, "lay": lay, "x_cpu": x_cpu, "wall_ms": wall_ms, "gpu_ms": gpu_ms, "eager_ms": eager_ms,
+            "stages": stages, "y": y, "logits": logits, "ids": ids}
 
 
 def bench_decode(cfg, n_steps, graph_chunk=32):
@@ -139,7 +153,7 @@ def bench_decode(cfg, n_steps, graph_chunk=32):
     layers = []
     for l in range(cfg.layers):
         lay = synth.make_layer(d, cfg.seed, layer=l, device="cuda")
-        layers.append(device_layer(lay, d, moe))
+        layers.append(device_layer(lay, d, moe, pack=False))   # T == 1 reads the canonical layout
     xs = torch.stack([synth.activations(1, d.hidden, cfg.seed, step=s)[0] for s in range(n_steps)]).cuda()
     ws = moe.moe_workspace(md, 1)
     ys = torch.empty((cfg.layers, d.hidden), dtype=torch.bfloat16, device="cuda")
@@ -183,7 +197,63 @@ def bench_decode(cfg, n_steps, graph_chunk=32):
             "workload": "decode T=1, 40 layers distinct seeded int4 weights, fresh x per step"}
 
 
-def cpu_baseline(res, sample, threads):
+GEMM_SOURCES = ("sparse_moe_softmax_amd/csrc/gemm.hip", "sparse_moe_softmax_amd/csrc/internal.hpp")
+TRAFFIC_PROFILE = "profiles/gemm_gate_up_t4096_hbm_traffic.md"
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter profile, if it
+    was taken on the current GEMM source (else None)."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_stage(cfg, stage, reps):
+    """Run the layer once, then one stage `reps` times, then a 256 MiB device
+    copy that calibrates the byte counters (profiling runs only)."""
+    import torch
+    import sparse_moe_softmax_amd as moe
+    import synth
+    d = cfg.dims
+    md = moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+    lay = synth.make_layer(d, cfg.seed, zipf_bias=cfg.zipf_bias, device="cuda")
+    dl = device_layer(lay, d, moe)
+    x = synth.activations(cfg.T, d.hidden, cfg.seed).cuda()
+    ws = moe.moe_workspace(md, cfg.T)
+    y = torch.empty((cfg.T, d.hidden), dtype=torch.bfloat16, device="cuda")
+    moe.moe_forward(md, dl, x, y=y, workspace=ws)
+    i = moe.STAGES.index(stage)
+    for _ in range(reps):
+        moe.moe_forward_stages(md, dl, x, y, ws, i, i)
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"profiled {stage} x{reps} on {cfg.name}, then {reps} copies of 256 MiB")
+
+
+def cpu_baseline(res, sample, threads, min_secs=10.0, max_passes=8):
     """The oracle, as it stands, on `sample` tokens of the same workload; also
     cross-checks those tokens' GPU outputs (shared-logits protocol)."""
     import numpy as np
@@ -196,13 +266,18 @@ def cpu_baseline(res, sample, threads):
     ow = oracle.LayerWeights(ln["gate_up"], ln["down"], ln["sh_gate_up"], ln["sh_down"], ln["router_w"],
                              ln["shared_gate_w"], ln["router_bias"])
     rng = np.random.default_rng(cfg.seed)
+    sample = min(sample, cfg.T)
     tok = np.sort(rng.choice(cfg.T, sample, replace=False)).astype(np.int32)
     xb = synth.bf16_bits_numpy(res["x_cpu"])[tok]
-    log(f"cpu baseline: oracle on {sample} of {cfg.T} tokens, {threads} threads")
+    log(f"cpu baseline: oracle on {sample} of {cfg.T} tokens, {threads} threads, repeated to >= {min_secs} s")
+    passes = 0
     t0 = time.perf_counter()
-    r = oracle.layer(od, xb, ow, threads=threads)
-    t1 = time.perf_counter()
-    secs = t1 - t0
+    while True:
+        r = oracle.layer(od, xb, ow, threads=threads)
+        passes += 1
+        if time.perf_counter() - t0 >= min_secs or passes >= max_passes:
+            break
+    secs = time.perf_counter() - t0
     # cross-check against the GPU: logits, ids given the GPU logits, and the outputs
     g_logits = res["logits"].cpu().numpy()[tok]
     g_ids = res["ids"].cpu().numpy()[tok]
@@ -216,9 +291,9 @@ def cpu_baseline(res, sample, threads):
     max_rel = float(np.abs(g - o).max() / np.abs(o).max())
     l1_rel = float(np.abs(g - o).sum() / np.abs(o).sum())
     log(f"cpu baseline: {secs:.2f} s; parity max_rel {max_rel:.2e} l1_rel {l1_rel:.2e} ids_equal {ids_equal}")
-    return ({"value": round(sample / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return ({"value": round(passes * sample / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
              "sample": f"{sample} of the {cfg.T} tokens of the same layer (router, top-k, experts incl. "
-                       f"dequantisation of the experts they touch, combine), {secs:.1f} s"},
+                       f"dequantisation of the experts they touch, combine), {passes} pass(es), {secs:.1f} s"},
             {"tokens": sample, "logit_max_abs_err": logit_err, "ids_equal_given_gpu_logits": ids_equal,
              "max_rel": max_rel, "l1_rel": l1_rel, "pass": bool(logit_err <= 1e-4 and ids_equal and
                                                                    max_rel <= 1e-2 and l1_rel <= 2e-3)})
@@ -233,8 +308,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--cpu-sample", type=int, default=4096)
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--profile-stage", default=None, help="profiling run: one stage repeated, no JSON line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -248,6 +324,9 @@ def main():
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[args.workload]
     d = cfg.dims
+    if args.profile_stage:
+        profile_stage(cfg, args.profile_stage, args.steps)
+        return
     res = bench_prefill(cfg, args.steps, args.warmup)
     T = cfg.T
     tok_s = T / (res["wall_ms"] / 1000.0)
@@ -274,10 +353,13 @@ def main():
                    "skewed_routing": cfg.zipf_bias, "seed": cfg.seed},
         "layer_mfma": {"flops_per_token": layer_flops_per_token(d), "achieved_tflops": round(layer_tflops, 2),
                        "frac_of_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
-                       "gpu_ms_per_step": round(res["gpu_ms"], 5)},
+                       "gpu_ms_per_step": round(res["gpu_ms"], 5),
+                       "launch": "whole layer as one HIP graph, replayed",
+                       "eager_ms_per_step": round(res["eager_ms"], 5)},
         "stages_us": {k: round(v, 2) for k, v in res["stages"].items()},
         "roofline": {"bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "k_gemm_q4<0> (gate/up grouped GEMM, SwiGLU epilogue, + shared expert)",
                      "flops_per_launch": gate_up_flops(d, T), "us_per_launch": round(gu_us, 2)},
     }
