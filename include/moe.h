@@ -210,9 +210,11 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
  * to each other through counters in the workspace (see moe_workspace_bytes;
  * needs hidden <= 4096, inter and shared_inter <= 1024); T > 1 runs
  * router GEMM, top-k, grouping, the two grouped GEMMs on the matrix cores
- * (needs router_w3 and the packed weights of all four matrices) and the combine: the down GEMM stores every slot's
- * weighted output in fp16 and a final pass sums each token's k+1 entries in
- * slot order (shared expert last) in fp32, so y is bitwise reproducible.
+ * (needs router_w3 and the packed weights of all four matrices) and the combine;
+ * the shared expert's tiles run in the same GEMM launches.  The down GEMM stores every
+ * routed slot's weighted output and the shared expert's output in fp16, and a
+ * final pass sums each token's k+1 entries in slot order (shared expert last,
+ * times the gate) in fp32, so y is bitwise reproducible.
  * No host synchronisation anywhere.
  * Optional outputs (NULL to skip): logits_out [T][E], ids_out [T][k], w_out [T][k].
  * workspace_bytes must be >= moe_workspace_bytes(d, T). */

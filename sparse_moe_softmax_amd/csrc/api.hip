@@ -319,7 +319,8 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   uint16_t* hsh = at<uint16_t>(workspace, w.hsh);
   const int E = d->n_experts, k = d->top_k;
   const int mt = moe_max_tiles(T, k, E, kBM);
-  GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM))};
+  // shared-expert chunks of kBM rows go first in the same launches as the routed tiles
+  const GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM))};
 
   // router output: final logits (one K split) or per-split partial sums that top-k adds up in order
   const int S = w.splits;
@@ -342,11 +343,13 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   if (run(MOE_STAGE_GATE_UP) &&
       (st = hip_check(launch_gemm_swiglu(*d, L->gate_up, &L->sh_gate_up, x, tl, T, h, hsh, s), "gate/up gemm")))
     return st;
+  // slots are stored unweighted; the combine applies routing weights and the gate
   if (run(MOE_STAGE_DOWN) &&
-      (st = hip_check(launch_gemm_slots(*d, L->down, &L->sh_down, h, hsh, tl, wts, gate, T, slots, s), "down gemm")))
+      (st = hip_check(launch_gemm_slots(*d, L->down, &L->sh_down, h, hsh, tl, nullptr, nullptr, T, slots, s),
+                      "down gemm")))
     return st;
   if (run(MOE_STAGE_COMBINE) &&
-      (st = hip_check(launch_combine(slots, y, T, d->hidden, k, s), "combine")))
+      (st = hip_check(launch_combine(slots, wts, gate, y, T, d->hidden, k, s), "combine")))
     return st;
   return MOE_OK;
 }

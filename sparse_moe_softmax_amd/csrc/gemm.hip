@@ -37,10 +37,11 @@
 //   SWIGLU : wave columns = 32 gate rows + the matching 32 up rows;
 //            h = bf16( silu(gate) * up ) in grouped order.
 //   SCATTER: y[token][col] += weight * o, fp32 atomics (standalone op).
-//   SLOTS  : slot[token][j][col] = fp16(weight * o): the weighted output of
-//            slot j of the token (routed: its routing weight; shared expert:
-//            slot k with the sigmoid gate), token-major, for a fixed-order
-//            combine afterwards.  No atomics.
+//   SLOTS  : slot[token][j][col] = fp16(weight * o): the output of slot j of
+//            the token (routed: times its routing weight; shared expert: slot
+//            k, times the sigmoid gate) or, without weights, fp16(o) for the
+//            combine to weight; token-major, for a fixed-order combine
+//            afterwards.  No atomics.
 //
 // Launch order is XCD-aware: consecutive workgroup ids go round-robin to the 8
 // XCDs, so ids are mapped such that all column slices of one tile share an XCD
@@ -114,7 +115,7 @@ struct Tile {
 // column lane%32.
 template <int MODE, int MT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsigned char* ring,
-                                          const int64_t* s_drow, const float* s_wt) {
+                                          int64_t* s_drow, float* s_wt) {
   constexpr int kAI = MT;                          // A direct loads per wave per stage (8 rows each)
   constexpr int kDma = kAI + 3;                   // + 2 code loads + scale/bias
   constexpr int kStages = Ring<MT>::kStages;
@@ -263,6 +264,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
     if (s < kg) issue(s);
+  // unweighted slots: this thread's row's flat slot, needed only at the epilogue
+  const bool deferred_rows = MODE == kSlots && g.row_w == nullptr;
+  int my_f = 0;
+  if (deferred_rows && t.which == 0 && static_cast<int>(threadIdx.x) < t.rows) my_f = g.perm[t.row0 + threadIdx.x];
   wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1));
   __builtin_amdgcn_s_barrier();
   bf16x8 b0[2][4], b1[2][4];
@@ -291,6 +296,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
   // 4 KB LDS area at the start of the ring, which is free once every wave has
   // left the loop; stores are then 16 contiguous bytes per lane.
   __syncthreads();
+  if (deferred_rows) {
+    const int r = threadIdx.x;
+    if (r < t.rows) {
+      const int k = g.k;
+      s_drow[r] = t.which == 1 ? static_cast<int64_t>(t.row0 + r) * (k + 1) + k
+                               : static_cast<int64_t>(my_f / k) * (k + 1) + (my_f % k);
+      s_wt[r] = 1.0f;
+    }
+    __syncthreads();
+  }
   if (!t.active) return;
   const int rows = t.rows, row0 = t.row0;
   unsigned char* stg = ring + wave * 4096;
@@ -408,17 +423,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(GemmArgs g) {
   t.pbase = g.packed[t.which] + static_cast<int64_t>(e) * g.expert_bytes[t.which] +
             static_cast<int64_t>(slice) * t.kg * kPackBlock;
 
-  // Output row and weight of every tile row (down projection epilogues), filled
-  // before the K loop; its first barrier publishes them.
+  // Output row and weight of every tile row (down projection epilogues).  With
+  // row weights (scatter, weighted slots) they are filled before the K loop,
+  // whose first barrier publishes them.  Unweighted slots need only the output
+  // row: gemm_tile loads the permutation after issuing its first stages and
+  // fills s_drow at the epilogue, so that load adds no latency to the start.
   __shared__ int64_t s_drow[kBM];
   __shared__ float s_wt[kBM];
-  if (MODE != kSwiglu) {
+  if (MODE != kSwiglu && !(MODE == kSlots && g.row_w == nullptr)) {
     for (int r = tid; r < t.rows; r += kGemmThreads) {
       const int k = g.k;
       if (t.which == 1) {
         const int tok = t.row0 + r;
         s_drow[r] = (MODE == kSlots) ? static_cast<int64_t>(tok) * (k + 1) + k : tok;
-        s_wt[r] = g.gate[tok];
+        s_wt[r] = g.gate ? g.gate[tok] : 1.0f;   // without a gate the combine applies it
       } else {
         const int f = g.perm[t.row0 + r];
         s_drow[r] = (MODE == kSlots) ? static_cast<int64_t>(f / k) * (k + 1) + (f % k) : f / k;
@@ -587,10 +605,12 @@ hipError_t launch_prepack_q4(const moe_dims& d, int matrix, const moe_q4& w, int
   return hipGetLastError();
 }
 
-// out[t][n] = bf16( sum_{j=0..k} slot[t][j][n] ), slots fp16, summed in fp32 in
-// slot order (shared expert last).  8 columns per thread.
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ slots, uint16_t* __restrict__ out,
-                                                 int T, int H, int k) {
+// out[t][n] = bf16( sum_{j<k} w[t][j] * slot[t][j][n] + gate[t] * slot[t][k][n] ),
+// slots fp16, summed in fp32 in slot order (shared expert last); w or gate
+// NULL = weights of 1 (slots already weighted).  8 columns per thread.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ slots, const float* __restrict__ w,
+                                                 const float* __restrict__ gate, uint16_t* __restrict__ out, int T,
+                                                 int H, int k) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 8-column group
   const int per_tok = H / 8;
   if (i >= static_cast<int64_t>(T) * per_tok) return;
@@ -602,10 +622,11 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
     const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
     const f16x2 p[4] = {__builtin_bit_cast(f16x2, v.x), __builtin_bit_cast(f16x2, v.y),
                         __builtin_bit_cast(f16x2, v.z), __builtin_bit_cast(f16x2, v.w)};
+    const float wj = j == k ? (gate ? gate[t] : 1.0f) : (w ? w[t * k + j] : 1.0f);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      acc[2 * u] += static_cast<float>(p[u].x);
-      acc[2 * u + 1] += static_cast<float>(p[u].y);
+      acc[2 * u] = __builtin_fmaf(wj, static_cast<float>(p[u].x), acc[2 * u]);
+      acc[2 * u + 1] = __builtin_fmaf(wj, static_cast<float>(p[u].y), acc[2 * u + 1]);
     }
   }
   uint4 o;
@@ -616,9 +637,11 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
   *reinterpret_cast<uint4*>(out + t * H + c8) = o;
 }
 
-hipError_t launch_combine(const uint16_t* slots, uint16_t* out, int T, int H, int k, hipStream_t s) {
+hipError_t launch_combine(const uint16_t* slots, const float* w, const float* gate, uint16_t* out, int T, int H, int k,
+                          hipStream_t s) {
   const int64_t n = static_cast<int64_t>(T) * (H / 8);
-  hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>(div_up(n, 256))), dim3(256), 0, s, slots, out, T, H, k);
+  hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>(div_up(n, 256))), dim3(256), 0, s, slots, w, gate, out, T,
+                     H, k);
   return hipGetLastError();
 }
 

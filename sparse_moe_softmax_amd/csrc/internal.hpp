@@ -356,8 +356,10 @@ hipError_t launch_gemm_scatter(const moe_dims& d, const moe_q4& w, const moe_q4*
 hipError_t launch_gemm_slots(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
                              const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate, int T,
                              uint16_t* slots, hipStream_t s);
-// out[t] = bf16( sum_j slot[t][j] ) in slot order.
-hipError_t launch_combine(const uint16_t* slots, uint16_t* out, int T, int H, int k, hipStream_t s);
+// out[t] = bf16( sum_{j<k} w[t][j] * slot[t][j] + gate[t] * slot[t][k] ) in slot order
+// (w or gate NULL = 1).
+hipError_t launch_combine(const uint16_t* slots, const float* w, const float* gate, uint16_t* out, int T, int H, int k,
+                          hipStream_t s);
 struct DecodePtrs {
   float* logits;
   float* s_logit;
