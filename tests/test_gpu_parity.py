@@ -317,6 +317,21 @@ def test_forward_parity_full(dname, T):
     say("errors", r["errs"])
 
 
+# hidden 512 / inter 256 / shared 384: the fewest K blocks the one-workgroup-per-CU
+# GEMM takes (4), a shared expert wider than the routed ones (routed gate/up
+# slices past the routed width are skipped) and more than one tile per
+# workgroup; hidden 320 takes the one-tile-per-workgroup GEMM (odd K blocks)
+@pytest.mark.parametrize("hidden,inter,shared,E,k,T", [(512, 256, 384, 64, 6, 300), (512, 256, 384, 64, 6, 2000),
+                                                         (320, 256, 128, 32, 4, 500)])
+def test_forward_parity_gemm_forms(hidden, inter, shared, E, k, T):
+    d = synth.Dims(hidden=hidden, inter=inter, n_experts=E, top_k=k, group_size=64, shared_inter=shared)
+    say("forward gemm forms", d, T)
+    lay = synth.make_layer(d, 5 + T)
+    x = synth.activations(T, d.hidden, 5 + T)
+    r = gu.forward_and_check(d, lay, x)
+    say("errors", r["errs"])
+
+
 @pytest.mark.parametrize("cfg", ["t4096", "skew16k"])
 def test_forward_parity_large_sampled(cfg):
     c = synth.CONFIGS[cfg]
