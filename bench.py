@@ -10,7 +10,9 @@ Headline (``value``): prefill tokens/s of one layer at T=4096 (hidden 2048,
 weights).  Also reported: the layer's fraction of dense bf16 MFMA peak, the
 dominant kernel's roofline (timed live with HIP events on the launch stream),
 per-stage times, batch-1 decode over 40 stacked layers x 256 steps as HBM GB/s,
-and the CPU oracle timed on a bounded token sample of the same workload.
+the GPU-resident vs host-synchronised routing ablation at T=512, a T=1..16
+small-batch sweep, and the CPU oracle timed on a bounded token sample of the
+same workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -197,6 +199,94 @@ def bench_decode(cfg, n_steps, graph_chunk=32):
             "workload": "decode T=1, 40 layers distinct seeded int4 weights, fresh x per step"}
 
 
+def bench_routing_ablation(cfg, steps, warmup):
+    """GPU-resident grouping (moe_forward) against the variant that takes the
+    expert counts through the host and builds offsets and block map there
+    (moe_forward_host_routing), eager launches, wall clock per layer."""
+    import torch
+    import sparse_moe_softmax_amd as moe
+    import synth
+    d = cfg.dims
+    md = moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+    lay = synth.make_layer(d, cfg.seed, zipf_bias=cfg.zipf_bias, device="cuda")
+    dl = device_layer(lay, d, moe)
+    x = synth.activations(cfg.T, d.hidden, cfg.seed).cuda()
+    ws = moe.moe_workspace(md, cfg.T)
+    hb = torch.empty(moe.moe_host_routing_bytes(md, cfg.T), dtype=torch.uint8, pin_memory=True)
+    y = torch.empty((cfg.T, d.hidden), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y)
+    runs = {"gpu_resident": lambda: moe.moe_forward(md, dl, x, y=y, workspace=ws),
+            "host_synchronised": lambda: moe.moe_forward_host_routing(md, dl, x, y=y2, workspace=ws, host_buf=hb)}
+    out = {}
+    for name, fn in runs.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        out[name] = (time.perf_counter() - t0) * 1e6 / steps
+    same = bool(torch.equal(y, y2))
+    log(f"routing ablation {cfg.name}: gpu-resident {out['gpu_resident']:.1f} us, host-synchronised "
+        f"{out['host_synchronised']:.1f} us per layer; outputs equal {same}")
+    return {"workload": f"moe_layer_prefill_{cfg.name}", "tokens": cfg.T,
+            "gpu_resident_us": round(out["gpu_resident"], 2), "host_synchronised_us": round(out["host_synchronised"], 2),
+            "speedup_of_gpu_resident": round(out["host_synchronised"] / out["gpu_resident"], 3),
+            "outputs_bitwise_equal": same, "timing": f"eager launches, wall clock, mean of {steps} layers"}
+
+
+def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20):
+    """Decode-like small batches: one pass over n_layers distinct layers per
+    replay (a HIP graph), algorithmic bytes = the experts the tokens touch +
+    shared expert + router + activations, per layer."""
+    import numpy as np
+    import torch
+    import sparse_moe_softmax_amd as moe
+    import synth
+    d = cfg.dims
+    md = moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+    layers = [device_layer(synth.make_layer(d, cfg.seed, layer=l, device="cuda"), d, moe) for l in range(n_layers)]
+    eb, sb = expert_bytes(d), expert_bytes(synth_dims_shared(d))
+    out = []
+    for T in Ts:
+        x = synth.activations(T, d.hidden, cfg.seed, step=T).cuda()
+        ws = moe.moe_workspace(md, T)
+        ys = torch.empty((n_layers, T, d.hidden), dtype=torch.bfloat16, device="cuda")
+        ids = torch.empty((n_layers, T, d.top_k), dtype=torch.int32, device="cuda")
+
+        def one_pass():
+            for l, dl in enumerate(layers):
+                moe.moe_forward(md, dl, x, y=ys[l], ids_out=ids[l], workspace=ws)
+
+        one_pass()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_pass()
+        g.replay()
+        torch.cuda.synchronize()
+        s_ = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s_)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s_)
+        torch.cuda.synchronize()
+        us_layer = e0.elapsed_time(e1) * 1000.0 / reps / n_layers
+        touched = [len(np.unique(ids[l].cpu().numpy())) for l in range(n_layers)]
+        bytes_layer = (float(np.mean(touched)) * eb + sb + d.n_experts * d.hidden * 4 + d.hidden * 4
+                       + 2 * T * d.hidden * 2)
+        gbs = bytes_layer / (us_layer * 1e-6) / 1e9
+        out.append({"T": T, "us_per_layer": round(us_layer, 3), "experts_touched": round(float(np.mean(touched)), 2),
+                    "bytes_per_layer": int(bytes_layer), "GBs": round(gbs, 1),
+                    "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                    "path": "fused GEMV layer" if T == 1 else "router GEMM, grouping, grouped GEMMs"})
+        log(f"small T={T}: {us_layer:.2f} us/layer, {out[-1]['experts_touched']} experts, {gbs:.0f} GB/s")
+    return {"layers": n_layers, "launch": f"HIP graph of one pass over {n_layers} layers, {reps} replays",
+            "points": out}
+
+
 GEMM_SOURCES = ("sparse_moe_softmax_amd/csrc/gemm.hip", "sparse_moe_softmax_amd/csrc/internal.hpp")
 TRAFFIC_PROFILE = "profiles/gemm_gate_up_t4096_hbm_traffic.md"
 
@@ -308,6 +398,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the routing ablation and the small-T sweep")
     ap.add_argument("--cpu-sample", type=int, default=4096)
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--profile-stage", default=None, help="profiling run: one stage repeated, no JSON line")
@@ -365,6 +456,9 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(synth.CONFIGS["decode"], args.decode_steps)
+    if not args.no_extras:
+        out["routing_ablation"] = bench_routing_ablation(synth.CONFIGS["t512"], max(20, args.steps), args.warmup)
+        out["small_t"] = bench_small_t(synth.CONFIGS["decode"])
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"], out["parity_sample"] = cpu_baseline(res, args.cpu_sample, threads)

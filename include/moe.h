@@ -212,9 +212,10 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
  * router GEMM, top-k, grouping, the two grouped GEMMs on the matrix cores
  * (needs router_w3 and the packed weights of all four matrices) and the combine;
  * the shared expert's tiles run in the same GEMM launches.  The down GEMM stores every
- * routed slot's weighted output and the shared expert's output in fp16, and a
- * final pass sums each token's k+1 entries in slot order (shared expert last,
- * times the gate) in fp32, so y is bitwise reproducible.
+ * routed slot's output and the shared expert's output in fp16, unweighted, and
+ * a final pass multiplies each of a token's k+1 entries by its routing weight
+ * (the shared one by the gate) and sums them in slot order in fp32, so y is
+ * bitwise reproducible.
  * No host synchronisation anywhere.
  * Optional outputs (NULL to skip): logits_out [T][E], ids_out [T][k], w_out [T][k].
  * workspace_bytes must be >= moe_workspace_bytes(d, T). */
@@ -224,8 +225,8 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t
 
 /* The stages of moe_forward, in order.  T > 1: router GEMM (partial sums over
  * K splits when T is small), top-k + tile histogram, grouping, gate/up grouped GEMM
- * (+ shared expert), down grouped GEMM writing the weighted slot outputs
- * (+ shared expert), combine to bf16.  T == 1: the fused layer runs as the
+ * (+ shared expert), down grouped GEMM writing the unweighted slot outputs
+ * (+ shared expert), weighted combine to bf16.  T == 1: the fused layer runs as the
  * ROUTER stage; the other stages are empty. */
 typedef enum moe_stage {
   MOE_STAGE_ROUTER = 0,
@@ -245,6 +246,33 @@ typedef enum moe_stage {
 moe_status moe_forward_stages(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,
                               float* logits_out, int32_t* ids_out, float* w_out, void* workspace,
                               size_t workspace_bytes, int32_t first, int32_t last, void* stream);
+
+/* Host-side offsets and block map from per-expert counts (no GPU involved):
+ * offsets[E+1] exclusive prefix sum, block_map[max_tiles][2] (expert, first
+ * row) for every tile of block_m rows, experts ascending, unused entries
+ * (-1, -1), *n_tiles used entries; the same values moe_group() computes on the
+ * GPU.  All pointers are host memory.  MOE_ERR_INVALID_ARG for a negative
+ * count, a sum past 2^31 or more tiles than max_tiles. */
+moe_status moe_host_block_map(const int32_t* counts, int32_t E, int32_t block_m, int32_t max_tiles, int32_t* offsets,
+                              int32_t* block_map, int32_t* n_tiles);
+
+/* Host bytes moe_forward_host_routing() needs for T tokens. */
+size_t moe_host_routing_bytes(const moe_dims* d, int32_t T);
+
+/* moe_forward (T > 1) with the routing round trip through the host that the
+ * pages removed (Inside Lily page, section "Key Optimizations at a Glance", GPU-resident
+ * expert routing): after top-k the per-expert counts are copied to the
+ * host, the stream is synchronised, offsets and block map are built on the
+ * host (moe_host_block_map) and copied back, and the permutation, GEMMs and
+ * combine follow as in moe_forward.  Same kernels and grouping, so y, ids and
+ * weights are bitwise those of moe_forward.  Measures what the GPU-resident
+ * grouping saves; it blocks the calling thread and cannot be captured into a
+ * graph.  host_buf: host memory of moe_host_routing_bytes(d, T) bytes (pinned
+ * memory keeps the copies asynchronous), reused across calls.  T == 1 is
+ * MOE_ERR_UNSUPPORTED. */
+moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T,
+                                    uint16_t* y, int32_t* ids_out, float* w_out, void* workspace,
+                                    size_t workspace_bytes, void* host_buf, size_t host_bytes, void* stream);
 
 /* Human-readable name of a status; message of the last failed check on this thread. */
 const char* moe_status_str(moe_status s);

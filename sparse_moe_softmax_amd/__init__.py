@@ -19,7 +19,7 @@ __all__ = [
     "Dims", "MoeError", "LayerWeights", "lib", "moe_block_m", "moe_max_tiles", "moe_prepack_router",
     "moe_router_logits", "moe_route", "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4",
     "moe_workspace_bytes", "moe_workspace", "moe_forward", "moe_forward_stages", "moe_packed_q4_bytes",
-    "moe_prepack_q4",
+    "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes", "moe_forward_host_routing",
     "MOE_EPI_SWIGLU_BF16",
     "MOE_EPI_WEIGHTED_SCATTER_F32", "STAGES",
     "EXPORTED_SYMBOLS",
@@ -36,7 +36,8 @@ EXPORTED_SYMBOLS = (
     "moe_block_m", "moe_max_tiles", "moe_prepack_router", "moe_router_logits", "moe_route",
     "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4", "moe_workspace_bytes", "moe_forward",
     "moe_forward_stages", "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
-    "moe_packed_q4_bytes", "moe_prepack_q4",
+    "moe_packed_q4_bytes", "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes",
+    "moe_forward_host_routing",
 )
 
 
@@ -101,6 +102,9 @@ def lib():
             "moe_last_hip_error": ([], _I32),
             "moe_packed_q4_bytes": ([PD, _I32, _I32], _SZ),
             "moe_prepack_q4": ([PD, _I32, ctypes.POINTER(_Q4), _I32, _P, _SZ, _P], _I32),
+            "moe_host_block_map": ([_P, _I32, _I32, _I32, _P, _P, _P], _I32),
+            "moe_host_routing_bytes": ([PD, _I32], _SZ),
+            "moe_forward_host_routing": ([PD, PL, _P, _I32, _P, _P, _P, _P, _SZ, _P, _SZ, _P], _I32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(h, name)
@@ -277,6 +281,45 @@ def moe_forward(d, layer: LayerWeights, x: torch.Tensor, y=None, logits_out=None
         workspace = moe_workspace(d, T, x.device)
     _check(lib().moe_forward(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y), _ptr(logits_out),
                              _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def moe_host_block_map(counts: torch.Tensor, block_m: int, max_tiles: int):
+    """Host offsets, block map and tile count from per-expert counts (CPU
+    int32 tensor of length E); returns (offsets [E+1], block_map [max_tiles][2], n_tiles)."""
+    if counts.is_cuda or counts.dtype != torch.int32:
+        raise ValueError("counts must be a CPU int32 tensor")
+    counts = counts.contiguous()
+    E = counts.numel()
+    offsets = torch.empty(E + 1, dtype=torch.int32)
+    block_map = torch.empty((max_tiles, 2), dtype=torch.int32)
+    n_tiles = torch.empty(1, dtype=torch.int32)
+    _check(lib().moe_host_block_map(counts.data_ptr(), E, block_m, max_tiles, offsets.data_ptr(), block_map.data_ptr(),
+                                    n_tiles.data_ptr()))
+    return offsets, block_map, int(n_tiles.item())
+
+
+def moe_host_routing_bytes(d, T: int) -> int:
+    return int(lib().moe_host_routing_bytes(ctypes.byref(_dims(d)), T))
+
+
+def moe_forward_host_routing(d, layer: LayerWeights, x: torch.Tensor, y=None, ids_out=None, w_out=None,
+                             workspace: torch.Tensor | None = None, host_buf: torch.Tensor | None = None):
+    """moe_forward with the routing counts taken through the host (blocks the
+    calling thread).  host_buf: a CPU uint8 tensor of moe_host_routing_bytes
+    bytes, pinned for asynchronous copies."""
+    T = x.shape[0]
+    if y is None:
+        y = _empty((T, d.hidden), torch.bfloat16, x)
+    if workspace is None:
+        workspace = moe_workspace(d, T, x.device)
+    if host_buf is None:
+        host_buf = torch.empty(moe_host_routing_bytes(d, T), dtype=torch.uint8, pin_memory=True)
+    if host_buf.is_cuda:
+        raise ValueError("host_buf must be host memory")
+    _check(lib().moe_forward_host_routing(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y),
+                                          _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(),
+                                          host_buf.data_ptr(), host_buf.numel(), _stream()))
     return y
 
 

@@ -2,6 +2,7 @@
 // sequence of every entry point.  Nothing here synchronises the host with the
 // device and nothing allocates device memory.
 #include <algorithm>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -358,6 +359,87 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* L, const uint16_t* x,
                        float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
                        void* stream) {
   return moe_forward_stages(d, L, x, T, y, logits_out, ids_out, w_out, workspace, workspace_bytes, MOE_STAGE_ROUTER,
+                            MOE_STAGE_COMBINE, stream);
+}
+
+moe_status moe_host_block_map(const int32_t* counts, int32_t E, int32_t block_m, int32_t max_tiles, int32_t* offsets,
+                              int32_t* block_map, int32_t* n_tiles) {
+  if (!counts || !offsets || !block_map || !n_tiles) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+  if (E < 1 || block_m < 1 || max_tiles < 0) return fail(MOE_ERR_INVALID_ARG, "E, block_m must be positive");
+  int64_t off = 0, tiles = 0;
+  for (int e = 0; e < E; ++e) {
+    if (counts[e] < 0) return fail(MOE_ERR_INVALID_ARG, "counts[%d] = %d is negative", e, counts[e]);
+    tiles += (counts[e] + block_m - 1) / block_m;
+    off += counts[e];
+    if (off > INT32_MAX) return fail(MOE_ERR_INVALID_ARG, "counts sum past 2^31");
+  }
+  if (tiles > max_tiles) return fail(MOE_ERR_INVALID_ARG, "max_tiles=%d < %lld tiles", max_tiles,
+                                     static_cast<long long>(tiles));
+  int32_t o = 0, t = 0;
+  for (int e = 0; e < E; ++e) {
+    offsets[e] = o;
+    for (int32_t r = 0; r < counts[e]; r += block_m, ++t) {
+      block_map[2 * t] = e;
+      block_map[2 * t + 1] = o + r;
+    }
+    o += counts[e];
+  }
+  offsets[E] = o;
+  *n_tiles = t;
+  for (int32_t i = t; i < max_tiles; ++i) block_map[2 * i] = block_map[2 * i + 1] = -1;
+  return MOE_OK;
+}
+
+size_t moe_host_routing_bytes(const moe_dims* d, int32_t T) {
+  if (check_dims(d) || check_T(T)) return 0;
+  const int E = d->n_experts;
+  return 4 * (static_cast<size_t>(E) + E + 1 + 2 * static_cast<size_t>(moe_max_tiles(T, d->top_k, E, kBM)) + 1);
+}
+
+moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* L, const uint16_t* x, int32_t T,
+                                    uint16_t* y, int32_t* ids_out, float* w_out, void* workspace,
+                                    size_t workspace_bytes, void* host_buf, size_t host_bytes, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  if (T == 1) return fail(MOE_ERR_UNSUPPORTED, "the host-routed variant covers T > 1 only");
+  const size_t need = moe_host_routing_bytes(d, T);
+  if (!host_buf || host_bytes < need) return fail(MOE_ERR_INVALID_ARG, "host buffer %zu < %zu bytes", host_bytes, need);
+  // router and top-k exactly as in moe_forward (this also validates the rest)
+  if ((st = moe_forward_stages(d, L, x, T, y, nullptr, ids_out, w_out, workspace, workspace_bytes, MOE_STAGE_ROUTER,
+                               MOE_STAGE_TOPK, stream)))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ws w = layout(*d, T);
+  const int E = d->n_experts, k = d->top_k;
+  const int mt = moe_max_tiles(T, k, E, kBM);
+  const int32_t* ids = ids_out ? ids_out : at<int32_t>(workspace, w.ids);
+  int32_t* counts = at<int32_t>(workspace, w.counts);
+  int32_t* offsets = at<int32_t>(workspace, w.offsets);
+  int32_t* bmap = at<int32_t>(workspace, w.bmap);
+  int32_t* ntiles = at<int32_t>(workspace, w.ntiles);
+  int32_t* tilebase = at<int32_t>(workspace, w.tilebase);
+  int32_t* h_counts = static_cast<int32_t*>(host_buf);
+  int32_t* h_offsets = h_counts + E;
+  int32_t* h_bmap = h_offsets + E + 1;
+  int32_t* h_ntiles = h_bmap + 2 * mt;
+  // counts to the host, wait, offsets + block map on the host, back to the GPU
+  if ((st = hip_check(launch_group_counts(at<int32_t>(workspace, w.tilehist), tilebase, T, E, counts, s),
+                      "expert counts")) ||
+      (st = hip_check(hipMemcpyAsync(h_counts, counts, 4 * E, hipMemcpyDeviceToHost, s), "counts to host")) ||
+      (st = hip_check(hipStreamSynchronize(s), "stream synchronize")))
+    return st;
+  if ((st = moe_host_block_map(h_counts, E, kBM, mt, h_offsets, h_bmap, h_ntiles))) return st;
+  if ((st = hip_check(hipMemcpyAsync(offsets, h_offsets, 4 * (E + 1), hipMemcpyHostToDevice, s), "offsets")) ||
+      (st = hip_check(hipMemcpyAsync(bmap, h_bmap, 8 * static_cast<size_t>(mt), hipMemcpyHostToDevice, s),
+                      "block map")) ||
+      (st = hip_check(hipMemcpyAsync(ntiles, h_ntiles, 4, hipMemcpyHostToDevice, s), "n_tiles")) ||
+      (st = hip_check(launch_group_scatter(ids, counts, tilebase, T, k, E, kBM, offsets,
+                                           at<int32_t>(workspace, w.perm), at<int32_t>(workspace, w.inv), bmap, mt,
+                                           ntiles, false, s),
+                      "permutation")))
+    return st;
+  return moe_forward_stages(d, L, x, T, y, nullptr, ids_out, w_out, workspace, workspace_bytes, MOE_STAGE_GATE_UP,
                             MOE_STAGE_COMBINE, stream);
 }
 

@@ -74,15 +74,16 @@ __global__ __launch_bounds__(256) void k_group_scan(const int32_t* __restrict__ 
 // running base[e] = offsets[e] + tilebase[b][e].  Wave 0 then walks the tile's
 // flat slots in order, 64 at a time: lanes with equal expert id find each
 // other through 8 ballots (one per id bit), the rank of a lane is the number
-// of matching lower lanes, and the group's count advances base[e].  Block 0
-// also writes offsets, the block map and n_tiles.
+// of matching lower lanes, and the group's count advances base[e].  With
+// write_map, block 0 also writes offsets, the block map and n_tiles (without,
+// the caller has put them there already).
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids,
                                                        const int32_t* __restrict__ counts,
                                                        const int32_t* __restrict__ tilebase, int T, int k, int E,
                                                        int block_m, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
                                                        int32_t* __restrict__ block_map, int max_tiles,
-                                                       int32_t* __restrict__ n_tiles) {
+                                                       int32_t* __restrict__ n_tiles, int write_map) {
   __shared__ int base[256];
   __shared__ int sm[4];
   const int tid = threadIdx.x;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
   const int off = block_excl_scan256(c, sm, &total);
   if (tid < E) base[tid] = off + tilebase[static_cast<int64_t>(blockIdx.x) * E + tid];
 
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0 && write_map) {
     const int nt = (c + block_m - 1) / block_m;
     int nt_total;
     const int toff = block_excl_scan256(nt, sm, &nt_total);
@@ -141,16 +142,29 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
   }
 }
 
+hipError_t launch_group_counts(const int32_t* tilehist, int32_t* tilebase, int T, int E, int32_t* counts,
+                               hipStream_t s) {
+  const int ntile = static_cast<int>(div_up(T, kTopkTile));
+  hipLaunchKernelGGL(k_group_scan, dim3(E), dim3(256), 0, s, tilehist, tilebase, ntile, E, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_scatter(const int32_t* ids, const int32_t* counts, const int32_t* tilebase, int T, int k,
+                                int E, int block_m, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map, hipStream_t s) {
+  const int ntile = static_cast<int>(div_up(T, kTopkTile));
+  hipLaunchKernelGGL(k_group_scatter, dim3(ntile), dim3(256), 0, s, ids, counts, tilebase, T, k, E, block_m, offsets,
+                     perm, inv_perm, block_map, max_tiles, n_tiles, write_map ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
                         int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                         int32_t* block_map, int max_tiles, int32_t* n_tiles, hipStream_t s) {
-  const int ntile = static_cast<int>(div_up(T, kTopkTile));
-  hipLaunchKernelGGL(k_group_scan, dim3(E), dim3(256), 0, s, tilehist, tilebase, ntile, E, counts);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_group_counts(tilehist, tilebase, T, E, counts, s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_group_scatter, dim3(ntile), dim3(256), 0, s, ids, counts, tilebase, T, k, E, block_m, offsets,
-                     perm, inv_perm, block_map, max_tiles, n_tiles);
-  return hipGetLastError();
+  return launch_group_scatter(ids, counts, tilebase, T, k, E, block_m, offsets, perm, inv_perm, block_map, max_tiles,
+                              n_tiles, true, s);
 }
 
 }  // namespace moe

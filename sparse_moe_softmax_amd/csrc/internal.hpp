@@ -344,6 +344,13 @@ hipError_t launch_topk(const float* parts, const float* s_parts, int splits, con
                        float* logits_out, float* s_out, int32_t* ids, float* wts, float* gate, int32_t* tilehist,
                        hipStream_t s);
 hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, hipStream_t s);
+// The two halves of launch_group: per-expert counts (and per-tile bases), then
+// offsets + permutation (+ block map and n_tiles when write_map).
+hipError_t launch_group_counts(const int32_t* tilehist, int32_t* tilebase, int T, int E, int32_t* counts,
+                               hipStream_t s);
+hipError_t launch_group_scatter(const int32_t* ids, const int32_t* counts, const int32_t* tilebase, int T, int k,
+                                int E, int block_m, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map, hipStream_t s);
 hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
                         int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                         int32_t* block_map, int max_tiles, int32_t* n_tiles, hipStream_t s);

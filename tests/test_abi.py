@@ -133,3 +133,61 @@ def test_binding_refuses_host_tensors(m):
     import torch
     with pytest.raises(ValueError):
         m.moe_route(m.Dims(), torch.zeros(4, 256))
+
+
+# ------------------------------------------------------------------ host-routed variant (host logic only)
+
+def _ids_for(T, E, k, mode, seed):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    if mode == "one_hot":
+        return np.tile(np.arange(k, dtype=np.int32) + 3, (T, 1))
+    p = None
+    if mode == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        p = p[rng.permutation(E)]
+        p /= p.sum()
+    return np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,bm,mode", [(512, 256, 8, 192, "uniform"), (300, 64, 6, 7, "zipf"),
+                                           (40, 16, 4, 1, "one_hot"), (4096, 256, 8, 192, "zipf")])
+def test_host_block_map_matches_oracle(m, T, E, k, bm, mode):
+    """The host builder of the routing round-trip variant gives the oracle's
+    offsets, block map and tile count."""
+    import numpy as np
+    import torch
+    import oracle
+    ids = _ids_for(T, E, k, mode, T + bm)
+    counts = torch.from_numpy(np.bincount(ids.reshape(-1), minlength=E).astype(np.int32))
+    mt = m.moe_max_tiles(T, k, E, bm)
+    offsets, bmap, nt = m.moe_host_block_map(counts, bm, mt)
+    ref = oracle.group(ids, E, bm, n_max_tiles=mt)
+    assert np.array_equal(offsets.numpy(), ref.offsets)
+    assert np.array_equal(bmap.numpy(), ref.block_map)
+    assert nt == ref.n_tiles
+
+
+def test_host_routing_checks(m):
+    L = m.lib()
+    E = 16
+    vp = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    off = (ctypes.c_int32 * (E + 1))()
+    bmap = (ctypes.c_int32 * 8)()
+    nt = (ctypes.c_int32 * 1)()
+    bad = (ctypes.c_int32 * E)(*([1] * (E - 1) + [-1]))
+    assert L.moe_host_block_map(vp(bad), E, 4, 4, vp(off), vp(bmap), vp(nt)) == -1      # negative count
+    many = (ctypes.c_int32 * E)(*([5] * E))
+    assert L.moe_host_block_map(vp(many), E, 4, 4, vp(off), vp(bmap), vp(nt)) == -1     # max_tiles too small
+    assert L.moe_host_block_map(None, E, 4, 4, vp(off), vp(bmap), vp(nt)) == -1
+    d = _d(m)
+    need = L.moe_host_routing_bytes(d, 512)
+    assert need == 4 * (256 + 257 + 2 * m.moe_max_tiles(512, 8, 256, m.moe_block_m()) + 1)
+    hb = (ctypes.c_uint8 * need)()
+    q = m._Q4(FAKE, FAKE, FAKE, FAKE)
+    layer = m._Layer(q, q, q, q, FAKE, None, FAKE, FAKE)
+    # T == 1 is not covered; a short host buffer is refused before any launch
+    assert L.moe_forward_host_routing(d, ctypes.byref(layer), FAKE, 1, FAKE, None, None, FAKE, 1 << 30, vp(hb), need,
+                                      None) == -2
+    assert L.moe_forward_host_routing(d, ctypes.byref(layer), FAKE, 512, FAKE, None, None, FAKE, 1 << 30, vp(hb),
+                                      need - 4, None) == -1

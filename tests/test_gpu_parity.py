@@ -307,7 +307,8 @@ def test_grouped_gemm_slots(dname, T, mode, bm):
 # ------------------------------------------------------------------ the whole layer
 
 @pytest.mark.parametrize("dname,T", [("tiny", 1), ("tiny", 2), ("tiny", 37), ("tiny", 129), ("model", 1),
-                                     ("model", 2), ("model", 3), ("model", 64), ("model", 127), ("model", 512)])
+                                     ("model", 2), ("model", 3), ("model", 4), ("model", 8), ("model", 16),
+                                     ("model", 64), ("model", 127), ("model", 512)])
 def test_forward_parity_full(dname, T):
     say("forward", dname, T)
     d = TINY if dname == "tiny" else MODEL
@@ -389,6 +390,30 @@ def test_decode_handover_words():
         assert int(words[256]) == 0                     # timeout word
     assert torch.equal(outs[0], outs[2]) and torch.equal(outs[0], outs[4])
     assert torch.equal(outs[1], outs[3]) and torch.equal(outs[1], outs[5])
+
+
+@pytest.mark.parametrize("T,cfg", [(2, None), (512, "t512"), (700, None), (4096, "skew16k")])
+def test_forward_host_routing_equals_forward(T, cfg):
+    """The variant that takes the expert counts through the host builds the same
+    offsets and block map there (pinned against the oracle on the CPU), so every
+    output is bitwise that of moe_forward."""
+    say("forward host routing T", T, cfg)
+    m = gu.moe()
+    d = MODEL
+    c = synth.CONFIGS[cfg] if cfg else None
+    lay = synth.make_layer(d, 91 + T, zipf_bias=bool(c and c.zipf_bias))
+    dl = gu.device_layer(lay, d)
+    md = gu.to_dims(d)
+    x = synth.activations(T, d.hidden, 91 + T).cuda()
+    ws_a, ws_b = m.moe_workspace(md, T), m.moe_workspace(md, T)
+    ids_a = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
+    ids_b = torch.empty_like(ids_a)
+    w_a = torch.empty((T, d.top_k), dtype=torch.float32, device="cuda")
+    w_b = torch.empty_like(w_a)
+    y_a = m.moe_forward(md, dl, x, ids_out=ids_a, w_out=w_a, workspace=ws_a)
+    y_b = m.moe_forward_host_routing(md, dl, x, ids_out=ids_b, w_out=w_b, workspace=ws_b)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_b) and torch.equal(w_a, w_b) and torch.equal(y_a, y_b)
 
 
 def test_forward_repeatable():
