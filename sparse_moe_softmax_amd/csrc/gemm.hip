@@ -28,10 +28,13 @@
 //     barrier per K block;
 //   * each wave reads its 64 columns' codes from LDS and dequantises them in
 //     registers into MFMA B fragments: exact fp32 c*s + b, one nearest-even
-//     rounding to bf16 (see dequant8), one K block ahead of the MFMAs that use
+//     rounding to bf16 (see dequant8), one k-step ahead of the MFMAs that use
 //     them.  Dequantised weights never reach LDS or HBM;
 //   * v_mfma_f32_32x32x16_bf16 with fp32 accumulators, every A fragment used
 //     for both 32-column groups of the wave.
+// Two workgroups run on each CU (half the LDS and at most 256 registers per
+// lane each), so that one workgroup's start-up latency, epilogue and stalls
+// are covered by the other's matrix work; tiles are at most 128 rows.
 //
 // Epilogues (through LDS so that every lane stores 16 contiguous bytes):
 //   SWIGLU : wave columns = 32 gate rows + the matching 32 up rows;
@@ -54,17 +57,18 @@ constexpr int kGemmThreads = 256;
 constexpr int kSliceRows = 256;                  // product columns (weight rows) per slice
 constexpr int kBStage = kSliceRows * 32;         // int4 codes of 256 weight rows x 64 K
 constexpr int kPackBlock = kBStage + kSliceRows * 4;  // + (fp16 scale, fp16 bias) per row = 9216 B
-constexpr int kRingBytes = 160 * 1024 - kBM * 12 - 512;  // LDS ring shared by all stages
+constexpr int kGemmOcc = 2;                      // workgroups per CU: LDS and registers are split
+constexpr int kRingBytes = (160 * 1024 / kGemmOcc - kBM * 12 - 512) / 256 * 256;  // LDS ring shared by all stages
 // A stage holds the live rows only (MT 32-row sub-tiles, 4 KB each); the
-// ring takes as many stages as fit, at most 8.
+// ring takes as many stages as fit, at most 8 (3 for a 128-row tile).
 template <int MT>
 struct Ring {
   static constexpr int kA = MT * 32 * 128;
   static constexpr int kStage = kA + kPackBlock;
   static constexpr int kStages = (kRingBytes / kStage) < 8 ? (kRingBytes / kStage) : 8;
-  static_assert(kStages >= 4, "ring too shallow");
+  static_assert(kStages >= 3, "ring too shallow");
 };
-static_assert(kRingBytes + kBM * 12 <= 160 * 1024, "LDS budget");
+static_assert(kRingBytes + kBM * 12 <= 160 * 1024 / kGemmOcc, "LDS budget");
 static_assert(kRingBytes % 256 == 0, "ring alignment");
 
 enum { kSwiglu = 0, kScatter = 1, kSlots = 2 };
@@ -209,58 +213,54 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
     }
   };
 
-  // One K block.  Entering iteration kb, stage kb has landed for every wave,
-  // its first A fragments are in af[0] and its dequantised weights in bcur.
-  // The iteration waits for its own loads of stage kb+1 and reads that
-  // stage's codes (a wave's codes and scales come only from its own loads, so
-  // they need no barrier), then barriers (stage kb+1 landed for every wave;
-  // stage kb-1 fully consumed), refills the slot of stage kb-1 with stage
-  // kb+kStages-1, and runs the MFMAs of stage kb while dequantising stage kb+1
-  // into bnext: the 8 dequantisations of a stage (2 column groups x 4
-  // k-steps) go one after each group of MT MFMAs, and the A fragments of the
-  // next k-step (of the next stage, after the last k-step) are read one k-step
-  // ahead; scheduling fences keep that interleaving.
-  // STEADY (kb + kStages - 1 < kg): the iteration always issues a stage and
-  // dequantises, and waits for a fixed count (one basic block).
   // Every wave computes, also an idle one (narrow shared expert, or N not a
   // multiple of the slice) on its dummy rows, whose results are never stored:
   // a branch here would make the compiler shuttle the accumulators between
   // register files on every K block.
   bf16x8 af[2][MT];
-  auto iteration = [&](auto steady_tag, int kb, bf16x8 (&bcur)[2][4], bf16x8 (&bnext)[2][4]) {
+  using Steady = std::integral_constant<bool, true>;
+  using Drain = std::integral_constant<bool, false>;
+
+  // One K block.  Two workgroups share a CU, so the other workgroup's wave on
+  // the same SIMD covers this one's stalls, and an iteration works on its own
+  // stage only: it waits for this wave's loads of stage kb (kStages - 2 later
+  // stages may stay in flight), barriers (stage kb landed for every wave;
+  // stage kb-1 fully consumed), refills the slot of stage kb-1 with stage
+  // kb + kStages - 1, reads the stage's codes, and runs the MFMAs with the
+  // dequantisation of each k-step's weights (2 column groups) one k-step ahead
+  // of the MFMAs that use them and the A fragments also read one k-step ahead;
+  // scheduling fences keep that interleaving.
+  // STEADY (kb + kStages - 1 < kg): the iteration always issues a stage and
+  // waits for a fixed count (one basic block).
+  auto iteration = [&](auto steady_tag, int kb) {
     constexpr bool kSteady = decltype(steady_tag)::value;
-    const bool more = kSteady || kb + 1 < kg;
-    // issued so far: stages 0 .. min(kb + kStages - 2, kg - 1); wait for stage kb+1
     if (kSteady)
-      wait_vmcnt<(kStages - 3) * kDma>();
-    else if (more)
-      wait_stages<kDma, kStages - 3>(min(kStages - 3, kg - 2 - kb));
-    BRaw raw;
-    if (more) read_b(kb + 1, raw);
-    __builtin_amdgcn_s_barrier();
+      wait_vmcnt<(kStages - 2) * kDma>();
+    else
+      wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1 - kb));
+    __builtin_amdgcn_s_barrier();   // stage kb landed for every wave; stage kb-1 consumed
     if (kSteady || kb + kStages - 1 < kg) issue(kb + kStages - 1);
     const unsigned char* st = ring + (kb % kStages) * kStageBytes;
-    const unsigned char* st_next = ring + ((kb + 1) % kStages) * kStageBytes;
+    BRaw raw;
+    read_b(kb, raw);
+    read_a(st, 0, af[0]);
+    bf16x8 bq[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) bq[0][c] = dq(raw, c, 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3)
-        read_a(st, ks + 1, af[(ks + 1) & 1]);
-      else if (more)
-        read_a(st_next, 0, af[0]);
+      if (ks < 3) read_a(st, ks + 1, af[(ks + 1) & 1]);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[ks & 1][m], bcur[c][ks], acc[m][c]);
-        if (more) bnext[c][ks] = dq(raw, c, ks);
+        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[ks & 1][m], bq[ks & 1][c], acc[m][c]);
+        if (ks < 3) bq[(ks + 1) & 1][c] = dq(raw, c, ks + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  using Steady = std::integral_constant<bool, true>;
-  using Drain = std::integral_constant<bool, false>;
 
-  // prologue: stages 0 .. kStages-2 in flight, stage 0 landed, dequantised and
-  // its first A fragments read
+  // prologue: stages 0 .. kStages-2 in flight
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
     if (s < kg) issue(s);
@@ -268,29 +268,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
   const bool deferred_rows = MODE == kSlots && g.row_w == nullptr;
   int my_f = 0;
   if (deferred_rows && t.which == 0 && static_cast<int>(threadIdx.x) < t.rows) my_f = g.perm[t.row0 + threadIdx.x];
-  wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1));
-  __builtin_amdgcn_s_barrier();
-  bf16x8 b0[2][4], b1[2][4];
-  {
-    BRaw raw;
-    read_b(0, raw);
-    read_a(ring, 0, af[0]);
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) b0[c][ks] = dq(raw, c, ks);
-  }
-  int kb = 0;
   const int steady_end = kg - (kStages - 1);   // iterations kb < steady_end are steady
-  for (; kb + 2 <= steady_end; kb += 2) {
-    iteration(Steady{}, kb, b0, b1);
-    iteration(Steady{}, kb + 1, b1, b0);
-  }
-  for (; kb + 2 <= kg; kb += 2) {
-    iteration(Drain{}, kb, b0, b1);
-    iteration(Drain{}, kb + 1, b1, b0);
-  }
-  if (kb < kg) iteration(Drain{}, kb, b0, b1);
+  int kb = 0;
+  for (; kb < steady_end; ++kb) iteration(Steady{}, kb);
+  for (; kb < kg; ++kb) iteration(Drain{}, kb);
 
   // ---- epilogue.  Each wave stages one 32-row sub-tile at a time in a private
   // 4 KB LDS area at the start of the ring, which is free once every wave has
@@ -376,7 +357,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_q4(GemmArgs g) {
+__global__ __launch_bounds__(kGemmThreads, kGemmOcc) void k_gemm_q4(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRingBytes];
 
   // ---- which tile / slice

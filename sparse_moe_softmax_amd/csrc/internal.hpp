@@ -21,10 +21,11 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// Tile height of the grouped GEMMs (rows of one block-map entry) and the
-// weight columns one wave owns.
+// Tile height of the grouped GEMMs (rows of one block-map entry).  128 rows
+// (four 32-row MFMA sub-tiles) is the most two workgroups per CU fit in
+// registers and LDS.
 #ifndef MOE_BM
-#define MOE_BM 192
+#define MOE_BM 128
 #endif
 constexpr int kBM = MOE_BM;
 static_assert(kBM % 32 == 0, "tile height: whole 32-row MFMA sub-tiles");
@@ -158,113 +159,71 @@ __device__ inline void wait_stages(int n) {
 __device__ inline int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 // ------------------------------------------------------------------ top-k (device helpers)
 
-// Top-k of one token's E logits by a group of 16 lanes.  Lane j holds the
-// logits of experts j, j+16, j+32, ...; each of the k rounds takes every
-// lane's best unselected logit and reduces over the group with the order
-// "larger logit first, then lower expert index".  Results are identical in
-// all 16 lanes: top_e[r], top_v[r] for r < k.
-// Top-k keys: the order "larger logit first, then lower expert index" as one
-// unsigned 64-bit comparison.  High half: the logit's bits mapped so that
-// unsigned order is float order (-0 folded into +0, so that they tie); low
-// half: ~expert.  Every key of a finite logit is > 0, so 0 means "none".
-__device__ inline uint64_t topk_key(float v, int e) {
-  uint32_t b = __float_as_uint(v + 0.0f);          // -0 + +0 = +0
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return (static_cast<uint64_t>(b) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+// Order-preserving 32-bit key of a logit (-0 folded onto +0): larger logit,
+// larger key; equal logits, equal keys.
+__device__ inline uint32_t topk_key32(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ inline float topk_key_value(uint64_t key) {
-  const uint32_t b = static_cast<uint32_t>(key >> 32);
+__device__ inline float topk_key32_value(uint32_t b) {
   return __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
 }
-__device__ inline int topk_key_expert(uint64_t key) {
-  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
-}
-// max(key, key of the partner lane under a DPP row permutation)
-template <int CTRL>
-__device__ inline uint64_t dpp_max(uint64_t key) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<uint32_t>(key), CTRL, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0, static_cast<uint32_t>(key >> 32), CTRL, 0xF, 0xF, false);
-  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-  return o > key ? o : key;
-}
-// max over a 16-lane DPP row (lane ^ 1, lane ^ 2, mirror within 8, mirror
-// within 16: afterwards every lane of the row holds the row maximum)
-__device__ inline uint64_t row_max16(uint64_t key) {
-  key = dpp_max<0xB1>(key);    // quad_perm [1,0,3,2]
-  key = dpp_max<0x4E>(key);    // quad_perm [2,3,0,1]
-  key = dpp_max<0x141>(key);   // row_half_mirror
-  return dpp_max<0x140>(key);  // row_mirror
+// max over a 16-lane DPP row (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror): afterwards every lane of the row holds it
+__device__ inline uint32_t row_max16_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  return max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
 }
 
-// Top-k of one token's logits by a group of 16 lanes that forms one DPP row
-// (lanes 16r .. 16r+15).  Each of the k rounds takes every lane's largest
-// remaining key, reduces over the row, and the lane that holds the winner
-// drops it (keys are unique).
-// CONTIG == false: lane j holds experts j, j+16, j+32, ... (v[i] = expert 16i + j);
-// CONTIG == true:  lane j holds experts nper*j .. nper*j + nper - 1 (v[i] = expert nper*j + i).
-template <bool CONTIG = false>
-__device__ inline void topk16_regs(const float (&v)[16], int nper, int k, int j, int (&top_e)[16],
-                                   float (&top_v)[16]) {
-  uint64_t key[16];
+// Top-k (k <= 16) of E <= 256 logits by one whole wave: lane l holds experts
+// l, l + 64, l + 128, l + 192.  Order: larger logit first, then lower expert
+// index (-0 and +0 tie).  Each of the k rounds finds the largest
+// remaining 32-bit key (per-lane max, DPP row max, max of the four rows in
+// scalar registers); among the lanes holding it, the lowest expert index wins
+// (the first slot i whose ballot is non-empty, then its lowest lane), and that
+// one entry is removed (key 0: real keys are >= 1).  Results are the same in
+// every lane.  v[i]: logit of expert lane + 64 i (ignored for experts >= E).
+__device__ inline void topk_wave64_regs(const float (&v)[4], int E, int k, int (&top_e)[16], float (&top_v)[16]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) key[i] = (i < nper) ? topk_key(v[i], CONTIG ? nper * j + i : i * 16 + j) : 0;
+  for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < E ? topk_key32(v[i]) : 0u;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r < k) {
-      uint64_t best = key[0];
+      uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
+      m = row_max16_u32(m);
+      uint32_t best = __builtin_amdgcn_readlane(m, 0);
+      best = max(best, static_cast<uint32_t>(__builtin_amdgcn_readlane(m, 16)));
+      best = max(best, static_cast<uint32_t>(__builtin_amdgcn_readlane(m, 32)));
+      best = max(best, static_cast<uint32_t>(__builtin_amdgcn_readlane(m, 48)));
+      int e = 0;
+      bool found = false;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) best = key[i] > best ? key[i] : best;
-      best = row_max16(best);
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t bal = __ballot(key[i] == best);
+        if (!found && bal != 0) {
+          e = 64 * i + static_cast<int>(__builtin_ctzll(bal));
+          found = true;
+        }
+      }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) key[i] = key[i] == best ? 0 : key[i];
-      top_e[r] = topk_key_expert(best);
-      top_v[r] = topk_key_value(best);
+      for (int i = 0; i < 4; ++i) key[i] = (lane + 64 * i == e) ? 0u : key[i];
+      top_e[r] = e;
+      top_v[r] = topk_key32_value(best);
     }
   }
 }
-
-// Top-k of E <= 256 logits (in LDS) by one whole wave: lane l holds experts
-// l, l + 64, l + 128, l + 192.  Rounds as in topk16_regs, with the four row
-// maxima combined through readlane.  Results are the same in every lane.
+// The same with the logits in memory (LDS).
 __device__ inline void topk_wave64(const float* __restrict__ logits, int E, int k, int (&top_e)[16],
                                    float (&top_v)[16]) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[4];
+  float v[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? topk_key(logits[e], e) : 0;
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r < k) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-      best = row_max16(best);
-      uint64_t w = best;
-#pragma unroll
-      for (int row = 0; row < 4; ++row) {
-        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(best), 16 * row);
-        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(best >> 32), 16 * row);
-        const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-        w = (row == 0 || o > w) ? o : w;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) key[i] = key[i] == w ? 0 : key[i];
-      top_e[r] = topk_key_expert(w);
-      top_v[r] = topk_key_value(w);
-    }
-  }
-}
-
-__device__ inline void topk16(const float* __restrict__ row, int E, int k, int j, int (&top_e)[16],
-                              float (&top_v)[16]) {
-  float v[16];
-  const int nper = E >> 4;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = (i < nper) ? row[i * 16 + j] : 0.f;
-  topk16_regs(v, nper, k, j, top_e, top_v);
+  for (int i = 0; i < 4; ++i) v[i] = lane + 64 * i < E ? logits[lane + 64 * i] : 0.f;
+  topk_wave64_regs(v, E, k, top_e, top_v);
 }
 
 // Renormalised weights of the k kept experts: exp(l_r - l_0) / sum_r' exp(l_r' - l_0),

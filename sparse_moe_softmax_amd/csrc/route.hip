@@ -229,110 +229,93 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* w, const float* bi
 
 // ------------------------------------------------------------------ top-k
 
-// One block = one routing tile of kTopkTile tokens, one group of 16 lanes per
-// token; lane j holds experts [16j, 16j + 16) (E / 16 of them), loaded as float4.
-// With several router splits the logits are first summed over the splits in
-// order (plus the bias) and written out.  Optionally counts the tile's expert
-// histogram.
-static_assert(kTopkTile * 16 == 256, "one 256-thread block per routing tile");
+// One block = one routing tile of kTopkTile tokens, one wave per token; lane l
+// holds experts l, l + 64, l + 128, l + 192 (coalesced loads).  With several
+// router splits the logits are first summed over the splits in order (plus the
+// bias) and written out.  Optionally counts the tile's expert histogram.
+constexpr int kTopkThreads = kTopkTile * 64;
 
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ parts, const float* __restrict__ s_parts,
-                                              int splits, const float* __restrict__ bias, int T, int E, int k,
-                                              float* __restrict__ logits_out, float* __restrict__ s_out,
-                                              int32_t* __restrict__ ids, float* __restrict__ wts,
-                                              float* __restrict__ gate, int32_t* __restrict__ tilehist) {
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ parts,
+                                                       const float* __restrict__ s_parts, int splits,
+                                                       const float* __restrict__ bias, int T, int E, int k,
+                                                       float* __restrict__ logits_out, float* __restrict__ s_out,
+                                                       int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                       float* __restrict__ gate, int32_t* __restrict__ tilehist) {
   __shared__ int hist[256];
   const int tid = threadIdx.x;
-  const int grp = tid >> 4, j = tid & 15;
+  const int lane = tid & 63;
+  const int t = blockIdx.x * kTopkTile + (tid >> 6);
   if (tilehist) {
-    for (int e = tid; e < E; e += 256) hist[e] = 0;
+    for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
     __syncthreads();
   }
-  const int t = blockIdx.x * kTopkTile + grp;
   if (t < T) {
-    const int nper = E >> 4;        // 1..16, a multiple of 4 when E % 64 == 0
     const int64_t TE = static_cast<int64_t>(T) * E;
-    const int64_t o = static_cast<int64_t>(t) * E + nper * j;
-    float v[16];
-    if ((nper & 3) == 0) {
-      float4 p[kMaxSplits][4];
+    const int64_t o = static_cast<int64_t>(t) * E;
+    // all partial sums are loaded first (one round trip), then added in split order
+    float p[kMaxSplits][4];
 #pragma unroll
-      for (int zz = 0; zz < kMaxSplits; ++zz)
-        if (zz < splits)
+    for (int zz = 0; zz < kMaxSplits; ++zz)
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (4 * c < nper) p[zz][c] = *reinterpret_cast<const float4*>(parts + zz * TE + o + 4 * c);
+      for (int i = 0; i < 4; ++i)
+        if (zz < splits && lane + 64 * i < E) p[zz][i] = parts[zz * TE + o + lane + 64 * i];
+    float v[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (4 * c < nper) {
-          float4 l = p[0][c];
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = 0.f;
+      if (e < E) {
+        float l = p[0][i];
 #pragma unroll
-          for (int zz = 1; zz < kMaxSplits; ++zz)
-            if (zz < splits) {
-              l.x += p[zz][c].x;
-              l.y += p[zz][c].y;
-              l.z += p[zz][c].z;
-              l.w += p[zz][c].w;
-            }
-          v[4 * c] = l.x;
-          v[4 * c + 1] = l.y;
-          v[4 * c + 2] = l.z;
-          v[4 * c + 3] = l.w;
+        for (int zz = 1; zz < kMaxSplits; ++zz)
+          if (zz < splits) l += p[zz][i];
+        if (splits > 1) {
+          if (bias) l += bias[e];
+          if (logits_out) logits_out[o + e] = l;
         }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i < nper) {
-          float l = parts[o + i];
-          for (int zz = 1; zz < splits; ++zz) l += parts[zz * TE + o + i];
-          v[i] = l;
-        }
+        v[i] = l;
       }
     }
-    if (splits > 1) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i < nper) {
-          if (bias) v[i] += bias[nper * j + i];
-          if (logits_out) logits_out[o + i] = v[i];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i >= nper) v[i] = 0.f;
     int te[16];
     float tv[16], w[16];
-    topk16_regs<true>(v, nper, k, j, te, tv);
+    topk_wave64_regs(v, E, k, te, tv);
     topk_weights(k, tv, w);
+    int my_e = 0;
+    float my_w = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (r < k && r == j) {
-        ids[static_cast<int64_t>(t) * k + r] = te[r];
-        wts[static_cast<int64_t>(t) * k + r] = w[r];
-        if (tilehist) atomicAdd(&hist[te[r]], 1);
+    for (int r = 0; r < 16; ++r)
+      if (r == lane) {
+        my_e = te[r];
+        my_w = w[r];
       }
+    if (lane < k) {
+      ids[static_cast<int64_t>(t) * k + lane] = my_e;
+      wts[static_cast<int64_t>(t) * k + lane] = my_w;
+      if (tilehist) atomicAdd(&hist[my_e], 1);
     }
-    if (s_parts && j == 0) {
-      float sl = s_parts[t];
-      if (splits > 1) {
-        for (int zz = 1; zz < splits; ++zz) sl += s_parts[static_cast<int64_t>(zz) * T + t];
-        if (s_out) s_out[t] = sl;
-      }
+    if (s_parts && lane == 0) {
+      float sp[kMaxSplits];
+#pragma unroll
+      for (int zz = 0; zz < kMaxSplits; ++zz)
+        if (zz < splits) sp[zz] = s_parts[static_cast<int64_t>(zz) * T + t];
+      float sl = sp[0];
+#pragma unroll
+      for (int zz = 1; zz < kMaxSplits; ++zz)
+        if (zz < splits) sl += sp[zz];
+      if (splits > 1 && s_out) s_out[t] = sl;
       if (gate) gate[t] = sigmoidf_(sl);
     }
   }
   if (tilehist) {
     __syncthreads();
-    for (int e = tid; e < E; e += 256) tilehist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
+    for (int e = tid; e < E; e += kTopkThreads) tilehist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
   }
 }
 
 hipError_t launch_topk(const float* parts, const float* s_parts, int splits, const float* bias, int T, int E, int k,
                        float* logits_out, float* s_out, int32_t* ids, float* wts, float* gate, int32_t* tilehist,
                        hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(static_cast<unsigned>(div_up(T, kTopkTile))), dim3(256), 0, s, parts, s_parts,
+  hipLaunchKernelGGL(k_topk, dim3(static_cast<unsigned>(div_up(T, kTopkTile))), dim3(kTopkThreads), 0, s, parts, s_parts,
                      splits, bias, T, E, k, logits_out, s_out, ids, wts, gate, tilehist);
   return hipGetLastError();
 }

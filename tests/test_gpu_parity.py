@@ -392,6 +392,40 @@ def test_decode_handover_words():
     assert torch.equal(outs[1], outs[3]) and torch.equal(outs[1], outs[5])
 
 
+@pytest.mark.parametrize("T", [1, 5, 300])
+def test_forward_router_ties(T):
+    """Duplicated router rows give bitwise-equal logits: for token 0 the top
+    expert's row is copied to a lower and a higher expert index (a three-way tie
+    for first place, which pushes the old 6th expert to 8th place) and that
+    expert's row to two others (a three-way tie across the cut).  The GPU ids must be the oracle's top-k of the GPU logits: lower expert
+    index first among equal logits, on the decode (T == 1) and prefill paths."""
+    say("forward router ties T", T)
+    d = MODEL
+    lay = synth.make_layer(d, 501 + T)
+    x = synth.activations(T, d.hidden, 501 + T)
+    ow = gu.oracle_layer(lay)
+    ol, _ = oracle.router(synth.bf16_bits_numpy(x)[:1], ow.router_w, ow.router_bias, ow.shared_gate_w)
+    order = [int(e) for e in np.argsort(-ol[0], kind="stable")]
+    top, eighth = order[0], order[5]
+    spare = [e for e in range(d.n_experts) if e not in order[:10]]
+    lo_t = min(spare)
+    hi_t = max(spare)
+    mid = [e for e in spare if e not in (lo_t, hi_t)]
+    a8, b8 = mid[0], mid[-1]
+    W = lay.router_w.clone()
+    W[lo_t] = W[top]
+    W[hi_t] = W[top]
+    W[a8] = W[eighth]
+    W[b8] = W[eighth]
+    lay = synth.Layer(lay.gate_up, lay.down, lay.sh_gate_up, lay.sh_down, W, lay.shared_gate_w, lay.router_bias)
+    r = gu.forward_and_check(d, lay, x)
+    gl = r["logits"][0]
+    assert gl[lo_t] == gl[top] == gl[hi_t] and gl[a8] == gl[eighth] == gl[b8]
+    first = sorted([lo_t, top, hi_t])
+    assert list(r["ids"][0][:3]) == first
+    say("ids of token 0", list(r["ids"][0]), "ties", first, sorted([a8, eighth, b8]))
+
+
 @pytest.mark.parametrize("T,cfg", [(2, None), (512, "t512"), (700, None), (4096, "skew16k")])
 def test_forward_host_routing_equals_forward(T, cfg):
     """The variant that takes the expert counts through the host builds the same
