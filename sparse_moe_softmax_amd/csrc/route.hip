@@ -168,22 +168,180 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
   }
 }
 
-int router_splits(int T, int H, int E) {
+// Wide form for large T: tiles of 128 tokens x 128 experts, 32-wide K blocks,
+// so that each weight plane row staged in LDS serves twice the tokens and each
+// x row twice the experts (half the bytes per flop of the 64 x 64 form).
+// 64-byte rows, 16-byte chunk c of row r stored at position c ^ ((r >> 2) & 3):
+// 16 consecutive rows read at one chunk hit 16 distinct bank groups.  Wave w
+// owns experts [32w, 32w + 32) for all 128 tokens (8 x 2 sub-tiles of
+// v_mfma_f32_16x16x32_bf16); lane group q = lane/16 covers K offsets
+// [8q, 8q + 8) of the block for both operands.  Shared gate, splits and
+// outputs as in the 64 x 64 form.
+constexpr int kRwM = 128;
+constexpr int kRwN = 128;
+constexpr int kRwStages = 4;
+constexpr int kRwX = kRwM * 64;                   // x tile: 128 rows x 32 K
+constexpr int kRwW = 3 * kRwN * 64;               // weight planes
+constexpr int kRwS = 4 * 256;                     // shared-gate weights (one copy per wave)
+constexpr int kRwStage = kRwX + kRwW + kRwS;
+constexpr int kRwDma = 2 + 6 + 1;                 // loads per wave per stage
+
+__device__ inline int rw_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(256) void k_router_gemm_wide(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w3,
+                                                          const float* __restrict__ bias,
+                                                          const float* __restrict__ wsg, int T, int H, int E,
+                                                          int kbs, float* __restrict__ out,
+                                                          float* __restrict__ s_out) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRwStages * kRwStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int col = lane & 15, q = lane >> 4;
+  const int t0 = blockIdx.x * kRwM;
+  const int rows = min(kRwM, T - t0);
+  const int e0 = blockIdx.y * kRwN;
+  const int z = blockIdx.z;
+  const int splits = gridDim.z;
+  const int kb0 = z * kbs;                         // first 32-wide K block of this split
+  const bool do_s = blockIdx.y == 0 && s_out != nullptr;
+
+  // per-lane load offsets (bytes): instruction j of wave w fills rows
+  // (2w + j) * 16 + lane/4, physical chunk lane % 4; rows past T or E re-read
+  // the last valid row
+  uint32_t xoff[2], woff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = (wave * 2 + j) * 16 + (lane >> 2);
+    const int c = rw_pos(r, lane & 3);             // the logical chunk stored at this position
+    xoff[j] = (static_cast<uint32_t>(t0 + min(r, rows - 1)) * H + kb0 * 32 + c * 8) * 2;
+    woff[j] = (static_cast<uint32_t>(min(e0 + r, E - 1)) * H + kb0 * 32 + c * 8) * 2;
+  }
+  const uint32_t plane_bytes = static_cast<uint32_t>(E) * H * 2;
+  const i32x4 xr = buffer_rsrc(x), wr = buffer_rsrc(w3), sr = buffer_rsrc(wsg);
+  const uint32_t soff = (kb0 * 32 + (lane & 31)) * 4;   // 32 weights per block, duplicated in the upper lanes
+  const uint32_t ring_s = lds_addr(ring);
+
+  auto issue = [&](int kb) {
+    const uint32_t st = ring_s + (kb % kRwStages) * kRwStage;
+    const uint32_t ko = kb * 64;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bdma16(xr, xoff[j], ko, st + (wave_s * 2 + j) * 1024);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bdma16(wr, woff[j] + p * plane_bytes, ko, st + kRwX + p * 8192 + (wave_s * 2 + j) * 1024);
+    bdma4(sr, soff, kb * 128, st + kRwX + kRwW + wave_s * 256);
+  };
+
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float s_acc = 0.f;
+  const int s_tok = tid >> 1, s_h = tid & 1;
+
+#pragma unroll
+  for (int st = 0; st < kRwStages - 1; ++st)
+    if (st < kbs) issue(st);
+  for (int kb = 0; kb < kbs; ++kb) {
+    // issued so far: stages 0 .. min(kb + kRwStages - 2, kbs - 1); wait for stage kb
+    wait_stages<kRwDma, kRwStages - 2>(min(kRwStages - 2, kbs - 1 - kb));
+    __builtin_amdgcn_s_barrier();  // stage kb landed for every wave; stage kb-1 consumed
+    if (kb + kRwStages - 1 < kbs) issue(kb + kRwStages - 1);
+    const unsigned char* st = ring + (kb % kRwStages) * kRwStage;
+    bf16x8 a[8], b[2][3];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int r = m * 16 + col;
+      a[m] = *reinterpret_cast<const bf16x8*>(st + r * 64 + (rw_pos(r, q) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int er = wave * 32 + j * 16 + col;
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        b[j][p] = *reinterpret_cast<const bf16x8*>(st + kRwX + p * 8192 + er * 64 + (rw_pos(er, q) << 4));
+    }
+#pragma unroll
+    for (int p = 2; p >= 0; --p)   // planes lo, mid, hi
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m][j] = mfma16(a[m], b[j][p], acc[m][j]);
+    if (do_s) {
+      const float* wsl = reinterpret_cast<const float*>(st + kRwX + kRwW);   // wave 0's copy
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * s_h + h;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(st + s_tok * 64 + (rw_pos(s_tok, c) << 4));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_acc = __builtin_fmaf(static_cast<float>(v[i]), wsl[c * 8 + i], s_acc);
+      }
+    }
+  }
+
+  const bool last = splits == 1;
+  float* o = out + static_cast<int64_t>(z) * T * E;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + wave * 32 + j * 16 + col;
+    if (e < E) {
+      const float b = (last && bias) ? bias[e] : 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m * 16 + q * 4 + i;
+          if (r < rows) o[static_cast<int64_t>(t0 + r) * E + e] = acc[m][j][i] + b;
+        }
+    }
+  }
+  if (do_s) {
+    s_acc += __shfl_xor(s_acc, 1);
+    if (s_h == 0 && s_tok < rows) s_out[static_cast<int64_t>(z) * T + t0 + s_tok] = s_acc;
+  }
+}
+
+// Tile form and K splits for T tokens: the wide form, unsplit, where its tiles
+// alone fill the chip (256 workgroups); else 64 x 64 tiles, split over K as
+// far as needed (at most kMaxSplits) to fill it.
+struct RouterPlan {
+  bool wide;
+  int splits;
+};
+static RouterPlan router_plan(int T, int H, int E) {
+  const int64_t wide_tiles = div_up(T, kRwM) * div_up(E, kRwN);
+  if (wide_tiles >= 256) return {true, 1};
   const int64_t tiles = div_up(T, kRtM) * div_up(E, kRtN);
   const int kg = H / 64;
   int want = static_cast<int>(div_up(256, tiles));
   want = want < 1 ? 1 : (want > kMaxSplits ? kMaxSplits : want);
   while (want > 1 && kg % want) --want;
-  return want;
+  return {false, want};
 }
+
+int router_splits(int T, int H, int E) { return router_plan(T, H, E).splits; }
 
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w3, const float* bias, const float* wsg, int T,
                               int H, int E, int splits, float* out, float* s_out, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>(div_up(T, kRtM)), static_cast<unsigned>(div_up(E, kRtN)),
-            static_cast<unsigned>(splits));
+  const RouterPlan plan = router_plan(T, H, E);
   const float* wsg_src = wsg ? wsg : reinterpret_cast<const float*>(w3);   // loaded but unused without s_out
-  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, w3, bias, wsg_src, T, H, E, H / 64 / splits, out,
-                     wsg ? s_out : nullptr);
+  if (plan.wide && splits == plan.splits) {
+    dim3 grid(static_cast<unsigned>(div_up(T, kRwM)), static_cast<unsigned>(div_up(E, kRwN)),
+              static_cast<unsigned>(splits));
+    hipLaunchKernelGGL(k_router_gemm_wide, grid, dim3(256), 0, s, x, w3, bias, wsg_src, T, H, E, H / 32 / splits,
+                       out, wsg ? s_out : nullptr);
+  } else {
+    dim3 grid(static_cast<unsigned>(div_up(T, kRtM)), static_cast<unsigned>(div_up(E, kRtN)),
+              static_cast<unsigned>(splits));
+    hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, x, w3, bias, wsg_src, T, H, E, H / 64 / splits, out,
+                       wsg ? s_out : nullptr);
+  }
   return hipGetLastError();
 }
 
