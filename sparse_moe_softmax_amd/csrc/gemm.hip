@@ -260,6 +260,40 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
     }
   };
 
+  // Short tiles (1-2 sub-tiles) have registers to spare, and their iteration
+  // is mostly fixed latency: there an iteration dequantises the NEXT stage's
+  // weights while the MFMAs use the current stage's (dequantised one
+  // iteration earlier), and waits for stage kb+1 instead of kb.
+  auto iteration_ahead = [&](auto steady_tag, int kb, bf16x8 (&bcur)[2][4], bf16x8 (&bnext)[2][4]) {
+    constexpr bool kSteady = decltype(steady_tag)::value;
+    const bool more = kSteady || kb + 1 < kg;
+    // issued so far: stages 0 .. min(kb + kStages - 2, kg - 1); wait for stage kb+1
+    if (kSteady)
+      wait_vmcnt<(kStages - 3) * kDma>();
+    else if (more)
+      wait_stages<kDma, kStages - 3>(min(kStages - 3, kg - 2 - kb));
+    BRaw raw;
+    if (more) read_b(kb + 1, raw);   // this wave's own loads: no barrier needed
+    __builtin_amdgcn_s_barrier();    // stage kb+1 landed for every wave; stage kb-1 consumed
+    if (kSteady || kb + kStages - 1 < kg) issue(kb + kStages - 1);
+    const unsigned char* st = ring + (kb % kStages) * kStageBytes;
+    const unsigned char* st_next = ring + ((kb + 1) % kStages) * kStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3)
+        read_a(st, ks + 1, af[(ks + 1) & 1]);
+      else if (more)
+        read_a(st_next, 0, af[0]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[ks & 1][m], bcur[c][ks], acc[m][c]);
+        if (more) bnext[c][ks] = dq(raw, c, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // prologue: stages 0 .. kStages-2 in flight
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
@@ -269,9 +303,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
   int my_f = 0;
   if (deferred_rows && t.which == 0 && static_cast<int>(threadIdx.x) < t.rows) my_f = g.perm[t.row0 + threadIdx.x];
   const int steady_end = kg - (kStages - 1);   // iterations kb < steady_end are steady
-  int kb = 0;
-  for (; kb < steady_end; ++kb) iteration(Steady{}, kb);
-  for (; kb < kg; ++kb) iteration(Drain{}, kb);
+  if constexpr (MT <= 2) {
+    static_assert(Ring<MT>::kStages >= 3, "the ahead loop waits one stage ahead");
+    // stage 0 landed, dequantised, and its first A fragments read
+    wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1));
+    __builtin_amdgcn_s_barrier();
+    bf16x8 b0[2][4], b1[2][4];
+    {
+      BRaw raw;
+      read_b(0, raw);
+      read_a(ring, 0, af[0]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) b0[c][ks] = dq(raw, c, ks);
+    }
+    int kb = 0;
+    for (; kb + 2 <= steady_end; kb += 2) {
+      iteration_ahead(Steady{}, kb, b0, b1);
+      iteration_ahead(Steady{}, kb + 1, b1, b0);
+    }
+    for (; kb + 2 <= kg; kb += 2) {
+      iteration_ahead(Drain{}, kb, b0, b1);
+      iteration_ahead(Drain{}, kb + 1, b1, b0);
+    }
+    if (kb < kg) iteration_ahead(Drain{}, kb, b0, b1);
+  } else {
+    int kb = 0;
+    for (; kb < steady_end; ++kb) iteration(Steady{}, kb);
+    for (; kb < kg; ++kb) iteration(Drain{}, kb);
+  }
 
   // ---- epilogue.  Each wave stages one 32-row sub-tile at a time in a private
   // 4 KB LDS area at the start of the ring, which is free once every wave has
