@@ -59,10 +59,25 @@ __device__ inline float dot8(uint32_t codes, const DqConst& dc, const uint4& xv,
   return acc;
 }
 
+template <int kCtrl>
+__device__ inline float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the wave, the same in every lane: a DPP sum within each row of 16
+// lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror: every lane of a row ends with the same value), then the four row
+// sums in a fixed order.  The whole wave must be active.
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Workspace words of the T == 1 path (zero before the first call).
@@ -102,18 +117,47 @@ __device__ inline uint64_t tagged(uint32_t tag, uint32_t payload) {
   return (static_cast<uint64_t>(tag) << 32) | payload;
 }
 
-// Read words[0 .. n) into out[] (payloads) until every word carries `tag`.
-__device__ inline void poll_words(const uint64_t* words, int n, uint32_t tag, uint32_t* out, uint32_t* timeout) {
+// Read the words i < n with live(i) into out[i] (payloads) until every one has
+// carried `tag`.  Thread t owns words t + kDecThreads * m, m < M: it requests
+// its pending words together, up to C at a time (so at most C owned words cost
+// one memory round trip per round), and a word once seen with the tag is not
+// requested again.  The block agrees
+// on "all done" with one barrier per round: wave w writes its verdict to
+// done[round & 1][w] (a wave cannot reach round r + 2's write before every wave
+// has passed round r + 1's barrier, that is, has read round r's verdicts).
+template <int M, int C, class Live>
+__device__ inline void poll_words(const uint64_t* words, int n, uint32_t tag, uint32_t* out, uint32_t* timeout,
+                                  Live live, uint32_t (&done)[2][kDecWaves]) {
+  const int tid = threadIdx.x;
+  uint32_t pending = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int i = tid + kDecThreads * m;
+    if (i < n && live(i)) pending |= 1u << m;
+  }
   for (uint32_t it = 0;; ++it) {
-    int ok = 1;
-    for (int i = threadIdx.x; i < n; i += kDecThreads) {
-      const uint64_t v = get(words + i);
-      ok &= static_cast<uint32_t>(v >> 32) == tag;
-      out[i] = static_cast<uint32_t>(v);
+#pragma unroll
+    for (int m0 = 0; m0 < M; m0 += C) {
+      uint64_t v[C];
+#pragma unroll
+      for (int m = m0; m < m0 + C && m < M; ++m)
+        if (pending >> m & 1u) v[m - m0] = get(words + tid + kDecThreads * m);
+#pragma unroll
+      for (int m = m0; m < m0 + C && m < M; ++m)
+        if ((pending >> m & 1u) && static_cast<uint32_t>(v[m - m0] >> 32) == tag) {
+          out[tid + kDecThreads * m] = static_cast<uint32_t>(v[m - m0]);
+          pending &= ~(1u << m);
+        }
     }
-    if (__syncthreads_and(ok)) return;
+    const bool wave_done = __ballot(pending != 0u) == 0;
+    if ((tid & 63) == 0) done[it & 1u][tid >> 6] = wave_done ? 1u : 0u;
+    __syncthreads();
+    uint32_t all = 1u;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) all &= done[it & 1u][w];
+    if (all) return;
     if (it >= kSpinLimit) {
-      if (threadIdx.x == 0) put(timeout, 1u);
+      if (tid == 0) put(timeout, 1u);
       return;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -202,16 +246,89 @@ __device__ inline float dot_dn(const DnRow<KCD>& r, const uint16_t* hrow, int K,
   return acc;
 }
 
-constexpr int kDecTasks = 2;    // routed gate/up (slot, column pair) tasks per wave and pass
+// routed gate/up (slot, column pair) tasks per wave and pass: two rows' loads in
+// flight where they fit the registers (hidden <= 2048), else one
+template <int KCG>
+constexpr int kDecTasks = KCG == 1 ? 2 : 1;
 constexpr int kDecMaxK = 16;
+constexpr int kDecMaxE = 256;
+static_assert(kDecMaxE + 1 <= kDecThreads, "one logit word per thread");
+static_assert(kDecMaxE == 32 * kDecWaves, "top-k stage 1 gives each wave 32 experts");
 
-template <int KCG, int KCD>
+// Top-k (k <= 16) of the E <= 256 logits (fp32 bits in l[]) by the whole
+// block, in the order larger logit first, then lower expert index (-0 and +0
+// tie).  Expert i's place in that order is fixed by a unique 64-bit key: the
+// order-preserving 32-bit image of its logit, then 255 - i (experts i >= E
+// get the key 255 - i, below every real one), so its rank is the number of
+// larger keys.
+//   1. wave w ranks experts 32w .. 32w + 31 among themselves, each half-wave
+//      counting against 16 of them; an expert outranked by k others of its
+//      own wave cannot be in the first k, so each wave passes on its first k;
+//   2. a survivor's overall rank is the number of larger survivors: wave w
+//      counts, for every survivor, the larger ones among wave w's k (for its
+//      own wave that count is its local rank), and the eight counts are
+//      summed; the survivor of rank r < k writes slot r (expert, logit).
+// Every thread of the block must call it; it ends with a barrier.
+__device__ inline void topk_block(const uint32_t* l, int E, int k, uint64_t* key, uint64_t* cand,
+                                  int (*part)[kDecWaves * kDecMaxK], int* top_e, float* top_v) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < kDecMaxE)
+    key[tid] = tid < E ? (static_cast<uint64_t>(topk_key32(__uint_as_float(l[tid]))) << 8) | (255u - tid)
+                       : static_cast<uint64_t>(255u - tid);
+  __syncthreads();
+  {
+    const uint64_t ki = key[32 * wv + (lane & 31)];
+    const uint64_t* kj = key + 32 * wv + 16 * (lane >> 5);
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r += kj[j] > ki ? 1 : 0;
+    r += __shfl_xor(r, 32);
+    if (lane < 32 && r < k) cand[wv * k + r] = ki;
+  }
+  __syncthreads();
+  const int nc = kDecWaves * k;
+  const uint64_t* mine = cand + wv * k;
+#pragma unroll
+  for (int c0 = 0; c0 < kDecWaves * kDecMaxK; c0 += 64) {
+    const int c = c0 + lane;
+    if (c0 < nc) {
+      int cnt = 0;
+      if (c < nc) {
+        const uint64_t kc = cand[c];
+#pragma unroll
+        for (int r = 0; r < kDecMaxK; ++r)
+          if (r < k) cnt += mine[r] > kc ? 1 : 0;
+      }
+      part[wv][c] = cnt;
+    }
+  }
+  __syncthreads();
+  if (tid < nc) {
+    int g = 0;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) g += part[w][tid];
+    if (g < k) {
+      const uint64_t kc = cand[tid];
+      top_e[g] = 255 - static_cast<int>(kc & 255u);
+      top_v[g] = topk_key32_value(static_cast<uint32_t>(kc >> 8));
+    }
+  }
+  __syncthreads();
+}
+
+// KMAX: bound on k the registers are sized for (8 or 16)
+template <int KCG, int KCD, int KMAX>
 __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t hs32[];  // h of all slots, [k+1][ldh/2] bf16 pairs
   __shared__ float red[2][kDecWaves];
   __shared__ int s_e[kDecMaxK];
-  __shared__ float s_w[kDecMaxK + 1];                              // [k] = shared gate
-  __shared__ uint32_t s_l[256 + 1];                                // logits, shared logit (fp32 bits)
+  __shared__ float s_v[kDecMaxK];                                  // top-k logits
+  __shared__ float s_w[kDecWaves][kDecMaxK + 1];                   // weights, [k] = shared gate; per wave
+  __shared__ uint32_t s_l[kDecMaxE + 1];                           // logits, shared logit (fp32 bits)
+  __shared__ uint64_t s_key[kDecMaxE];
+  __shared__ uint64_t s_cand[kDecWaves * kDecMaxK];
+  __shared__ int s_part[kDecWaves][kDecWaves * kDecMaxK];
+  __shared__ uint32_t s_done[2][kDecWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
@@ -298,43 +415,67 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
   }
 
   // ---- D: routing decision (every block)
-  poll_words(lw, E + 1, tag, s_l, &sy->timeout);
-  if (wv == 0) {
-    int te[16];
-    float tv[16], w[16];
-    topk_wave64(reinterpret_cast<const float*>(s_l), E, k, te, tv);
-    topk_weights(k, tv, w);
+  poll_words<1, 1>(lw, E + 1, tag, s_l, &sy->timeout, [](int) { return true; },
+                                                     s_done);
+  topk_block(s_l, E, k, s_key, s_cand, s_part, s_e, s_v);
+  // renormalised weights exp(l_r - l_0) / sum_r' exp(l_r' - l_0), the sum in
+  // slot order: lane r takes slot r's exponential.  Every wave computes them
+  // (the same values) into its own row of s_w, so no further barrier is
+  // needed; [k] = shared gate
+  float* sw = s_w[wv];
+  {
+    const float ex = lane < k ? expf(s_v[lane] - s_v[0]) : 0.f;
+    float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r == lane && r < k) {
-        s_e[r] = te[r];
-        s_w[r] = w[r];
-      }
-    if (lane == 0) s_w[k] = sigmoidf_(__uint_as_float(s_l[E]));
+    for (int r = 0; r < kDecMaxK; ++r)
+      if (r < k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), r));
+    const float inv = 1.0f / sum;
+    if (lane < k) sw[lane] = ex * inv;
+    if (lane == 0) sw[k] = sigmoidf_(__uint_as_float(s_l[E]));
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's s_w row is written
+  __builtin_amdgcn_wave_barrier();
   if (blockIdx.x == 0) {
     for (int i = tid; i < E; i += kDecThreads) a.logits[i] = __uint_as_float(s_l[i]);
     if (tid == 0) a.s_logit[0] = __uint_as_float(s_l[E]);
     if (tid < k) {
       a.ids[tid] = s_e[tid];
-      a.wts[tid] = s_w[tid];
+      a.wts[tid] = sw[tid];
     }
-    if (tid == 0) a.gate[0] = s_w[k];
+    if (tid == 0) a.gate[0] = sw[k];
   }
 
-  // ---- E + F: routed gate/up column pairs, task q = slot * (I/2) + pair
+  // ---- E + F: routed gate/up column pairs, task q = slot * (I/2) + pair.
+  // With hidden <= 2048 this wave's routed down rows are requested right after
+  // its first gate/up rows, so they arrive while h is being produced and
+  // handed over (wider rows leave no registers for that: there they follow
+  // the gate/up work).
   const int ip = I / 2;
   const int n_tasks = k * ip;
-  for (int q0 = gw; q0 < n_tasks; q0 += NW * kDecTasks) {
-    GuPair<KCG> ru[kDecTasks];
+  DnRow<KCD> dr[kRowsMax][KMAX];
+  auto load_down = [&]() {
 #pragma unroll
-    for (int t = 0; t < kDecTasks; ++t) {
+    for (int i = 0; i < kRowsMax; ++i) {
+      const int n = gw + NW * i;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (n < H && j < k) load_dn<KCD>(a.dn, s_e[j], I, n, H, lane, dr[i][j]);
+    }
+  };
+  bool down_issued = false;
+  for (int q0 = gw; q0 < n_tasks; q0 += NW * kDecTasks<KCG>) {
+    GuPair<KCG> ru[kDecTasks<KCG>];
+#pragma unroll
+    for (int t = 0; t < kDecTasks<KCG>; ++t) {
       const int q = q0 + NW * t;
       if (q < n_tasks) load_gu<KCG>(a.gu, s_e[q / ip], I, q % ip, H, lane, ru[t]);
     }
+    if (KCG == 1 && !down_issued) {
+      load_down();
+      down_issued = true;
+    }
 #pragma unroll
-    for (int t = 0; t < kDecTasks; ++t) {
+    for (int t = 0; t < kDecTasks<KCG>; ++t) {
       const int q = q0 + NW * t;
       if (q < n_tasks) {
         const uint32_t hv = swiglu_pair<KCG>(ru[t], xv, H, lane);
@@ -342,37 +483,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
       }
     }
   }
-  // routed down rows of this wave (issued before waiting for h)
-  DnRow<KCD> dr[kRowsMax][kDecMaxK];
-#pragma unroll
-  for (int i = 0; i < kRowsMax; ++i) {
-    const int n = gw + NW * i;
-#pragma unroll
-    for (int j = 0; j < kDecMaxK; ++j)
-      if (n < H && j < k) load_dn<KCD>(a.dn, s_e[j], I, n, H, lane, dr[i][j]);
-  }
+  if (!down_issued) load_down();
 
   // ---- G: all of h, then down GEMV and combine
-  {
-    const int nw = (k + 1) * hp;
-    for (uint32_t it = 0;; ++it) {
-      int ok = 1;
-      for (int i = tid; i < nw; i += kDecThreads) {
-        const int j = i / hp, pp = i % hp;
-        if (pp < (j < k ? ip : Is / 2)) {
-          const uint64_t v = get(hw + i);
-          ok &= static_cast<uint32_t>(v >> 32) == tag;
-          hs32[i] = static_cast<uint32_t>(v);
-        }
-      }
-      if (__syncthreads_and(ok)) break;
-      if (it >= kSpinLimit) {
-        if (tid == 0) put(&sy->timeout, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
+  constexpr int kHWords = (KMAX + 1) * 256 * KCD;   // k + 1 slots of at most 512 KCD columns
+  constexpr int kHPerThread = (kHWords + kDecThreads - 1) / kDecThreads;
+  // (the widest form, k > 8 with hidden and inter both past 2048 / 512, has no
+  // registers to spare: there one word is requested at a time)
+  constexpr int kHChunk = KCG * KCD == 4 && KMAX > 8 ? 1 : (kHPerThread < 9 ? kHPerThread : 9);
+  poll_words<kHPerThread, kHChunk>(
+      hw, (k + 1) * hp, tag, hs32, &sy->timeout,
+      [&](int i) {
+        const int j = i / hp;
+        return i - j * hp < (j < k ? ip : Is / 2);
+      },
+      s_done);
   const uint16_t* hs = reinterpret_cast<const uint16_t*>(hs32);
 #pragma unroll
   for (int i = 0; i < kRowsMax; ++i) {
@@ -380,9 +505,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
     if (n < H) {
       float yv = 0.f;
 #pragma unroll
-      for (int j = 0; j < kDecMaxK; ++j)
-        if (j < k) yv = __builtin_fmaf(s_w[j], dot_dn<KCD>(dr[i][j], hs + j * a.ldh, I, lane), yv);
-      yv = __builtin_fmaf(s_w[k], dot_dn<KCD>(dsh[i], hs + k * a.ldh, Is, lane), yv);
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) yv = __builtin_fmaf(sw[j], dot_dn<KCD>(dr[i][j], hs + j * a.ldh, I, lane), yv);
+      yv = __builtin_fmaf(sw[k], dot_dn<KCD>(dsh[i], hs + k * a.ldh, Is, lane), yv);
       yv = wave_sum(yv);
       if (lane == 0) a.y[n] = f32_to_bf16_bits(yv);
     }
@@ -403,7 +528,10 @@ size_t decode_sync_bytes(const moe_dims& d) {
 
 template <int KCG, int KCD>
 static void launch_dec(const DecArgs& a, size_t shbytes, hipStream_t s) {
-  hipLaunchKernelGGL((k_decode_layer<KCG, KCD>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
+  if (a.k <= 8)
+    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, 8>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
+  else
+    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, kDecMaxK>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
 }
 
 hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y,

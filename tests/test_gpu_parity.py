@@ -369,6 +369,22 @@ def test_decode_layers():
             gu.forward_and_check(c.dims, lay, x)
 
 
+# every register form of the fused T == 1 layer: hidden past 2048, inter past
+# 512, k past 8, and a ragged one (hidden 192: most lanes hold no K; 48
+# experts: the last top-k wave holds 16 real experts and 16 absent ones)
+@pytest.mark.parametrize("hidden,inter,shared,E,k", [(4096, 1024, 1024, 32, 12), (2048, 1024, 512, 64, 4),
+                                                     (4096, 256, 512, 16, 8), (1024, 512, 512, 256, 16),
+                                                     (192, 128, 64, 48, 5)])
+def test_decode_forms(hidden, inter, shared, E, k):
+    d = synth.Dims(hidden=hidden, inter=inter, n_experts=E, top_k=k, group_size=64, shared_inter=shared)
+    say("decode form", d)
+    lay = synth.make_layer(d, 7 + hidden + E)
+    for step in (0, 1):
+        x = synth.activations(1, d.hidden, 7 + hidden + E, step=step)
+        r = gu.forward_and_check(d, lay, x)
+        say("errors", r["errs"])
+
+
 def test_decode_handover_words():
     """The fused T == 1 layer passes logits and h between its workgroups in
     tagged words at the start of the workspace: after n calls every block has
