@@ -281,7 +281,7 @@ def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20):
         out.append({"T": T, "us_per_layer": round(us_layer, 3), "experts_touched": round(float(np.mean(touched)), 2),
                     "bytes_per_layer": int(bytes_layer), "GBs": round(gbs, 1),
                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                    "path": "fused GEMV layer" if T == 1 else "router GEMM, grouping, grouped GEMMs"})
+                    "path": "fused layer, one launch" if T <= 4 else "router GEMM, grouping, grouped GEMMs"})
         log(f"small T={T}: {us_layer:.2f} us/layer, {out[-1]['experts_touched']} experts, {gbs:.0f} GB/s")
     return {"layers": n_layers, "launch": f"HIP graph of one pass over {n_layers} layers, {reps} replays",
             "points": out}

@@ -67,7 +67,7 @@ typedef struct moe_dims {
  * down matrices:    N = H, K = I.
  * `packed` is the same weights in the matrix-core layout written by
  * moe_prepack_q4() (NULL if not prepared): the grouped GEMMs read only it, the
- * T == 1 path reads only the canonical arrays. */
+ * fused path for 1-4 tokens reads only the canonical arrays. */
 typedef struct moe_q4 {
   const uint8_t* codes;
   const uint16_t* scales;
@@ -105,10 +105,10 @@ typedef struct moe_layer {
   moe_q4 down;                 /* routed experts, [E][H][I] */
   moe_q4 sh_gate_up;           /* shared expert, [1][2Is][H] */
   moe_q4 sh_down;              /* shared expert, [1][H][Is] */
-  const float* router_w;       /* [E][H] fp32; read by the T == 1 path */
+  const float* router_w;       /* [E][H] fp32; read by the fused path (1-4 tokens) */
   const float* router_bias;    /* [E] fp32 added to the logits, or NULL */
   const float* shared_gate_w;  /* [H] fp32 */
-  const uint16_t* router_w3;   /* [3][E][H] bf16 from moe_prepack_router(); required when T > 1 */
+  const uint16_t* router_w3;   /* [3][E][H] bf16 from moe_prepack_router(); required by the grouped path */
 } moe_layer;
 
 /* Tile height (rows) that moe_forward uses for its block map. */
@@ -196,21 +196,24 @@ moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue 
                                const int32_t* n_tiles, int32_t max_tiles, const float* row_weight, int32_t T,
                                int32_t block_m, void* out, void* stream);
 
-/* Scratch bytes moe_forward() needs for up to T_max tokens.  The first 256
- * bytes hold the synchronisation counters of the T == 1 path: they must be
- * zero before a workspace's first T == 1 call (allocate it zero-filled), and
- * every call leaves them zero. */
+/* Scratch bytes moe_forward() needs for up to T_max tokens.  The workspace
+ * starts with the hand-over words of the fused path (1-4 tokens): per-block
+ * counts of completed calls and tagged data words.  They must be zero before a
+ * workspace's first fused call (allocate it zero-filled); after that every
+ * fused call keeps them consistent, and the grouped path never writes them. */
 size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
 
 /* The whole layer for T tokens:
  *   y[t] = bf16( sum_j w[t][j] * E_{ids[t][j]}(x[t]) + g[t] * E_shared(x[t]) ),
  *   E(x) = ( silu(x.Wg^T) * (x.Wu^T) ) . Wd^T with the SwiGLU product rounded to bf16.
- * T == 1 runs the decode path: one launch for the whole layer (vector-ALU
- * GEMV on the canonical weights, fp32 router_w), whose workgroups hand results
- * to each other through counters in the workspace (see moe_workspace_bytes;
- * needs hidden <= 4096, inter and shared_inter <= 1024); T > 1 runs
- * router GEMM, top-k, grouping, the two grouped GEMMs on the matrix cores
- * (needs router_w3 and the packed weights of all four matrices) and the combine;
+ * T == 1 (and 2 <= T <= 4 with hidden <= 2048, inter and shared_inter <= 512,
+ * k <= 8) runs the fused decode path: one launch for the whole layer
+ * (vector-ALU GEMV on the canonical weights, fp32 router_w), whose workgroups
+ * hand results to each other through words in the workspace (see
+ * moe_workspace_bytes; T == 1 needs hidden <= 4096, inter and shared_inter <=
+ * 1024).  Larger T runs router GEMM, top-k, grouping, the two grouped GEMMs on
+ * the matrix cores (needs router_w3 and the packed weights of all four
+ * matrices) and the combine;
  * the shared expert's tiles run in the same GEMM launches.  The down GEMM stores every
  * routed slot's output and the shared expert's output in fp16, unweighted, and
  * a final pass multiplies each of a token's k+1 entries by its routing weight
@@ -223,11 +226,12 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t
                        float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
-/* The stages of moe_forward, in order.  T > 1: router GEMM (partial sums over
+/* The stages of moe_forward, in order.  Grouped path: router GEMM (partial sums over
  * K splits when T is small), top-k + tile histogram, grouping, gate/up grouped GEMM
  * (+ shared expert), down grouped GEMM writing the unweighted slot outputs
- * (+ shared expert), weighted combine to bf16.  T == 1: the fused layer runs as the
- * ROUTER stage; the other stages are empty. */
+ * (+ shared expert), weighted combine to bf16.  Fused path (1-4 tokens, see
+ * moe_forward): the whole layer runs as the ROUTER stage; the other stages are
+ * empty. */
 typedef enum moe_stage {
   MOE_STAGE_ROUTER = 0,
   MOE_STAGE_TOPK = 1,
@@ -259,7 +263,7 @@ moe_status moe_host_block_map(const int32_t* counts, int32_t E, int32_t block_m,
 /* Host bytes moe_forward_host_routing() needs for T tokens. */
 size_t moe_host_routing_bytes(const moe_dims* d, int32_t T);
 
-/* moe_forward (T > 1) with the routing round trip through the host that the
+/* moe_forward (grouped path) with the routing round trip through the host that the
  * pages removed (Inside Lily page, section "Key Optimizations at a Glance", GPU-resident
  * expert routing): after top-k the per-expert counts are copied to the
  * host, the stream is synchronised, offsets and block map are built on the
@@ -268,8 +272,8 @@ size_t moe_host_routing_bytes(const moe_dims* d, int32_t T);
  * weights are bitwise those of moe_forward.  Measures what the GPU-resident
  * grouping saves; it blocks the calling thread and cannot be captured into a
  * graph.  host_buf: host memory of moe_host_routing_bytes(d, T) bytes (pinned
- * memory keeps the copies asynchronous), reused across calls.  T == 1 is
- * MOE_ERR_UNSUPPORTED. */
+ * memory keeps the copies asynchronous), reused across calls.  A T that
+ * moe_forward runs on the fused path (1-4 tokens) is MOE_ERR_UNSUPPORTED. */
 moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T,
                                     uint16_t* y, int32_t* ids_out, float* w_out, void* workspace,
                                     size_t workspace_bytes, void* host_buf, size_t host_bytes, void* stream);

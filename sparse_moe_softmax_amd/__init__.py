@@ -268,7 +268,7 @@ def moe_workspace_bytes(d, T_max: int) -> int:
 
 def moe_workspace(d, T_max: int, device="cuda") -> torch.Tensor:
     """A zero-filled workspace for moe_forward with up to T_max tokens (the
-    T == 1 path keeps counters in it that must start at zero)."""
+    fused path for 1-4 tokens keeps counters in it that must start at zero)."""
     return torch.zeros((moe_workspace_bytes(d, T_max),), dtype=torch.uint8, device=device)
 
 

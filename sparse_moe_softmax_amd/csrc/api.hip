@@ -91,7 +91,7 @@ Ws layout(const moe_dims& d, int32_t T) {
     o = align256(o + bytes);
     return at;
   };
-  w.sync = take(decode_sync_bytes(d));   // T == 1 hand-over words: first, never written by the T > 1 path
+  w.sync = take(decode_sync_bytes(d));   // fused-path hand-over words: first, never written by the grouped path
   w.logits = take(T * E * 4);
   w.s = take(T * 4);
   w.splits = T > 1 ? router_splits(T, d.hidden, d.n_experts) : 1;
@@ -282,7 +282,10 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   if (!L || !x || !y) return fail(MOE_ERR_INVALID_ARG, "NULL layer, x or y");
   if (first < MOE_STAGE_ROUTER || last > MOE_STAGE_COMBINE || first > last)
     return fail(MOE_ERR_INVALID_ARG, "stage range [%d, %d] invalid", first, last);
-  auto chk = T == 1 ? check_q4 : check_packed;   // the GEMV path reads canonical, the GEMMs packed weights
+  // up to kDecMaxT tokens run as one fused launch on the canonical weights; the
+  // grouped GEMMs read the packed ones
+  const bool fused = T <= kDecMaxT && decode_supported(*d, T);
+  auto chk = fused ? check_q4 : check_packed;
   if ((st = chk(&L->gate_up, "gate_up")) || (st = chk(&L->down, "down")) || (st = chk(&L->sh_gate_up, "sh_gate_up")) ||
       (st = chk(&L->sh_down, "sh_down")))
     return st;
@@ -290,11 +293,11 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   const Ws w = layout(*d, T);
   if (!workspace || workspace_bytes < w.total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, w.total);
-  if (T == 1 && !L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
-  if (T == 1 && !decode_supported(*d))
+  if (fused && !L->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+  if (T == 1 && !fused)
     return fail(MOE_ERR_UNSUPPORTED, "T == 1 needs hidden <= 4096, inter and shared_inter <= 1024");
-  if (T > 1 && !L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
-  if (T > 1 && (st = check_gemm_extent(*d, T))) return st;
+  if (!fused && !L->router_w3) return fail(MOE_ERR_INVALID_ARG, "router_w3 is NULL (run moe_prepack_router)");
+  if (!fused && (st = check_gemm_extent(*d, T))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* logits = logits_out ? logits_out : at<float>(workspace, w.logits);
   int32_t* ids = ids_out ? ids_out : at<int32_t>(workspace, w.ids);
@@ -303,10 +306,10 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   float* gate = at<float>(workspace, w.gate);
   auto run = [&](int stage) { return first <= stage && stage <= last; };
 
-  if (T == 1) {
-    // one fused launch for the whole layer, run as the ROUTER stage
+  if (fused) {
+    // one launch for the whole layer, run as the ROUTER stage
     DecodePtrs p{logits, s_logit, ids, wts, gate, at<void>(workspace, w.sync)};
-    if (run(MOE_STAGE_ROUTER)) return hip_check(launch_decode_layer(*d, *L, x, y, p, s), "decode layer");
+    if (run(MOE_STAGE_ROUTER)) return hip_check(launch_decode_layer(*d, *L, x, T, y, p, s), "fused layer");
     return MOE_OK;
   }
   uint16_t* slots = at<uint16_t>(workspace, w.slots);
@@ -402,7 +405,8 @@ moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* L, const
   moe_status st = check_dims(d);
   if (st) return st;
   if ((st = check_T(T))) return st;
-  if (T == 1) return fail(MOE_ERR_UNSUPPORTED, "the host-routed variant covers T > 1 only");
+  if (T <= kDecMaxT && decode_supported(*d, T))
+    return fail(MOE_ERR_UNSUPPORTED, "the host-routed variant covers the grouped path only (T=%d runs fused)", T);
   const size_t need = moe_host_routing_bytes(d, T);
   if (!host_buf || host_bytes < need) return fail(MOE_ERR_INVALID_ARG, "host buffer %zu < %zu bytes", host_bytes, need);
   // router and top-k exactly as in moe_forward (this also validates the rest)

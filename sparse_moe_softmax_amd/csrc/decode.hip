@@ -1,25 +1,27 @@
-// Batch-1 decode path of the MoE layer.  With one token per step every weight
-// is used once, so the work is matrix-vector, limited by memory bandwidth, and
-// the pages assign it to the vector ALUs rather than the matrix units (Lily
-// page, section "Why Apple Silicon isn't just a smaller datacenter GPU"); chains
-// of kernels are fused so that intermediates stay on chip (Inside Lily page,
-// section "Performance Gains and Workload Patterns").
+// Decode path of the MoE layer: one token per step, or a few (up to kDecMaxT,
+// the shapes of speculative verification).  Each touched expert's weights are
+// then used once per token, so the work is matrix-vector, limited by memory
+// bandwidth, and the pages assign it to the vector ALUs rather than the
+// matrix units (Lily page, section "Why Apple Silicon isn't just a smaller
+// datacenter GPU"); chains of kernels are fused so that intermediates stay on
+// chip (Inside Lily page, section "Performance Gains and Workload Patterns").
 //
 // The whole layer is one launch of kDecBlocks workgroups of 8 waves, all
 // resident at once:
 //   A. issue the loads that need no routing decision: this block's router
 //      row(s), the shared expert's gate/up rows of this wave's column pair and
 //      its down rows for this wave's output row;
-//   B. router dot products (fp32 weights)              -> logit words
-//   C. shared expert SwiGLU column pair                 -> h words of slot k
+//   B. router dot products (fp32 weights) of every token -> logit words
+//   C. shared expert SwiGLU column pair, every token    -> h words of slot k
 //   D. every block polls the logit words until all carry this call's tag and
-//      recomputes top-k itself (one wave, lower expert index on ties), so the
-//      routing decision needs no second round trip;
-//   E. issue the routed experts' gate/up rows of this wave's (slot, column
-//      pair) task and their down rows for this wave's output row;
+//      recomputes every token's top-k itself (all waves, lower expert index
+//      on ties), so the routing decision needs no second round trip;
+//   E. issue the routed experts' gate/up rows of this wave's (token, slot,
+//      column pair) task and the down rows of every token's experts for this
+//      wave's output row;
 //   F. routed SwiGLU column pairs                       -> h words of slot j
-//   G. poll the h words; down GEMV over the k+1 slots with the weighted
-//      combine in registers, slot order, shared expert last -> y (bf16).
+//   G. poll the h words; down GEMV over each token's k+1 slots with the
+//      weighted combine in registers, slot order, shared expert last -> y.
 // Int4 rows are dequantised in registers exactly as in the grouped GEMM
 // (bf16 of the exact fp32 c*s + b) and multiplied with v_dot2_f32_bf16.
 // No atomics on data: y is bitwise reproducible.
@@ -36,7 +38,7 @@
 // workgroups of one launch are all resident (kDecBlocks <= CUs, one block fits
 // a CU), so every wait ends; a wait that exceeds kSpinLimit polls sets the
 // timeout word and carries on, so a launch always completes.
-#include "internal.hpp"
+#include "gemv.hpp"
 
 namespace moe {
 
@@ -45,47 +47,12 @@ constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr uint32_t kSpinLimit = 1u << 22;
 
-__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-// 8 int4 weights of one group (one dword of codes) dotted with 8 bf16 (uint4).
-__device__ inline float dot8(uint32_t codes, const DqConst& dc, const uint4& xv, float acc) {
-  const uint4 w = dequant8(codes, dc.s24, dc.s20, dc.bias);
-  acc = dot2(w.x, xv.x, acc);
-  acc = dot2(w.y, xv.y, acc);
-  acc = dot2(w.z, xv.z, acc);
-  acc = dot2(w.w, xv.w, acc);
-  return acc;
-}
-
-template <int kCtrl>
-__device__ inline float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-
-// Sum over the wave, the same in every lane: a DPP sum within each row of 16
-// lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
-// row_mirror: every lane of a row ends with the same value), then the four row
-// sums in a fixed order.  The whole wave must be active.
-__device__ inline float wave_sum(float v) {
-  v += dpp_f32<0xB1>(v);
-  v += dpp_f32<0x4E>(v);
-  v += dpp_f32<0x141>(v);
-  v += dpp_f32<0x140>(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-// Workspace words of the T == 1 path (zero before the first call).
+// Workspace words of the fused path (zero before the first call).
 struct DecSync {
   uint32_t gen[kDecBlocks];   // calls completed, per block
   uint32_t timeout;
   uint32_t pad[63];
-  uint64_t words[1];          // logit words [E + 1], then h words [k + 1][ldh / 2]
+  uint64_t words[1];          // logit words [T][E + 1], then h words [T][k + 1][ldh / 2]
 };
 
 struct DecArgs {
@@ -93,15 +60,15 @@ struct DecArgs {
   const float* router_w;   // [E][H]
   const float* router_bias;
   const float* wsg;        // [H]
-  int H, I, Is, E, k;
-  const uint16_t* x;       // [H] bf16
-  float* logits;           // [E]
-  float* s_logit;          // [1]
-  int32_t* ids;            // [k]
-  float* wts;              // [k]
-  float* gate;             // [1]
+  int H, I, Is, E, k, T;
+  const uint16_t* x;       // [T][H] bf16
+  float* logits;           // [T][E]
+  float* s_logit;          // [T]
+  int32_t* ids;            // [T][k]
+  float* wts;              // [T][k]
+  float* gate;             // [T]
   int ldh;                 // h row stride (multiple of 8)
-  uint16_t* y;             // [H] bf16
+  uint16_t* y;             // [T][H] bf16
   DecSync* sync;
 };
 
@@ -162,88 +129,6 @@ __device__ inline void poll_words(const uint64_t* words, int n, uint32_t tag, ui
     }
     __builtin_amdgcn_s_sleep(1);
   }
-}
-
-// Gate/up rows of two adjacent h columns (2p, 2p+1) of one expert: rows
-// gate 2p, gate 2p+1, up 2p, up 2p+1; KCG chunks of 32 K per lane.
-template <int KCG>
-struct GuPair {
-  uint4 c[4][KCG];
-  uint16_t s[4][KCG], b[4][KCG];
-};
-
-template <int KCG>
-__device__ inline void load_gu(const moe_q4& q, int64_t e, int Ih, int p, int H, int lane, GuPair<KCG>& r) {
-  const int64_t base = e * 2 * static_cast<int64_t>(Ih);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int64_t row = base + (g >> 1) * Ih + 2 * p + (g & 1);
-#pragma unroll
-    for (int c = 0; c < KCG; ++c) {
-      const int k0 = 32 * lane + 2048 * c;
-      if (k0 < H) {
-        r.c[g][c] = *reinterpret_cast<const uint4*>(q.codes + row * (H / 2) + k0 / 2);
-        r.s[g][c] = q.scales[row * (H / 64) + k0 / 64];
-        r.b[g][c] = q.biases[row * (H / 64) + k0 / 64];
-      }
-    }
-  }
-}
-
-// bf16(silu(gate) * up) of both columns against x (KCG x 4 uint4 per lane),
-// packed (column 2p in the low half); the same in every lane.
-template <int KCG>
-__device__ inline uint32_t swiglu_pair(const GuPair<KCG>& r, const uint4 (&xv)[KCG][4], int H, int lane) {
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int c = 0; c < KCG; ++c)
-      if (32 * lane + 2048 * c < H) {
-        const DqConst dc = dq_const(r.s[g][c], r.b[g][c]);
-        acc[g] = dot8(r.c[g][c].x, dc, xv[c][0], acc[g]);
-        acc[g] = dot8(r.c[g][c].y, dc, xv[c][1], acc[g]);
-        acc[g] = dot8(r.c[g][c].z, dc, xv[c][2], acc[g]);
-        acc[g] = dot8(r.c[g][c].w, dc, xv[c][3], acc[g]);
-      }
-  float v[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) v[g] = wave_sum(acc[g]);
-  const float h0 = v[0] / (1.0f + __expf(-v[0])) * v[2];
-  const float h1 = v[1] / (1.0f + __expf(-v[1])) * v[3];
-  return pack_bf16x2(h0, h1);
-}
-
-// One down row of one slot, KCD chunks of 8 K per lane.
-template <int KCD>
-struct DnRow {
-  uint32_t c[KCD];
-  uint16_t s[KCD], b[KCD];
-};
-
-template <int KCD>
-__device__ inline void load_dn(const moe_q4& q, int64_t e, int K, int n, int H, int lane, DnRow<KCD>& r) {
-  const int64_t row = e * H + n;
-#pragma unroll
-  for (int c = 0; c < KCD; ++c) {
-    const int k0 = 8 * lane + 512 * c;
-    if (k0 < K) {
-      r.c[c] = *reinterpret_cast<const uint32_t*>(q.codes + row * (K / 2) + k0 / 2);
-      r.s[c] = q.scales[row * (K / 64) + k0 / 64];
-      r.b[c] = q.biases[row * (K / 64) + k0 / 64];
-    }
-  }
-}
-
-template <int KCD>
-__device__ inline float dot_dn(const DnRow<KCD>& r, const uint16_t* hrow, int K, int lane) {
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < KCD; ++c) {
-    const int k0 = 8 * lane + 512 * c;
-    if (k0 < K) acc = dot8(r.c[c], dq_const(r.s[c], r.b[c]), *reinterpret_cast<const uint4*>(hrow + k0), acc);
-  }
-  return acc;
 }
 
 // routed gate/up (slot, column pair) tasks per wave and pass: two rows' loads in
@@ -316,15 +201,16 @@ __device__ inline void topk_block(const uint32_t* l, int E, int k, uint64_t* key
   __syncthreads();
 }
 
-// KMAX: bound on k the registers are sized for (8 or 16)
-template <int KCG, int KCD, int KMAX>
+// KMAX: bound on k the registers are sized for (8 or 16); TM: bound on the
+// number of tokens (1, or kDecMaxT for the multi-token form).
+template <int KCG, int KCD, int KMAX, int TM>
 __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t hs32[];  // h of all slots, [k+1][ldh/2] bf16 pairs
-  __shared__ float red[2][kDecWaves];
-  __shared__ int s_e[kDecMaxK];
-  __shared__ float s_v[kDecMaxK];                                  // top-k logits
-  __shared__ float s_w[kDecWaves][kDecMaxK + 1];                   // weights, [k] = shared gate; per wave
-  __shared__ uint32_t s_l[kDecMaxE + 1];                           // logits, shared logit (fp32 bits)
+  extern __shared__ __attribute__((aligned(16))) uint32_t hs32[];  // h of all slots, [T][k+1][ldh/2] bf16 pairs
+  __shared__ float red[2][TM][kDecWaves];
+  __shared__ int s_e[TM][kDecMaxK];
+  __shared__ float s_v[TM][kDecMaxK];                              // top-k logits
+  __shared__ float s_w[kDecWaves][TM][kDecMaxK + 1];               // weights, [k] = shared gate; per wave
+  __shared__ uint32_t s_l[TM][kDecMaxE + 1];                       // logits, shared logit (fp32 bits)
   __shared__ uint64_t s_key[kDecMaxE];
   __shared__ uint64_t s_cand[kDecWaves * kDecMaxK];
   __shared__ int s_part[kDecWaves][kDecWaves * kDecMaxK];
@@ -336,27 +222,33 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
   const int NW = G * kDecWaves;
   const int gw = blockIdx.x * kDecWaves + wv;
   const int H = a.H, I = a.I, Is = a.Is, E = a.E, k = a.k;
+  const int T = TM == 1 ? 1 : a.T;
   const int hp = a.ldh / 2;                   // h words per slot
   DecSync* sy = a.sync;
   const uint32_t tag = get(&sy->gen[blockIdx.x]) + 1u;
-  uint64_t* lw = sy->words;                   // [E + 1]
-  uint64_t* hw = lw + (E + 1);                // [k + 1][hp]
+  uint64_t* lw = sy->words;                   // [T][E + 1]
+  uint64_t* hw = lw + T * (E + 1);            // [T][k + 1][hp]
 
   // ---- A: loads independent of routing
-  uint4 xv[KCG][4];   // x in the gate/up lane layout: K = [32 lane + 2048 c, +32)
+  uint4 xv[TM][KCG][4];   // x in the gate/up lane layout: K = [32 lane + 2048 c, +32)
 #pragma unroll
-  for (int c = 0; c < KCG; ++c)
-    if (32 * lane + 2048 * c < H)
+  for (int t = 0; t < TM; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[c][i] = *reinterpret_cast<const uint4*>(a.x + 32 * lane + 2048 * c + 8 * i);
+    for (int c = 0; c < KCG; ++c)
+      if (t < T && 32 * lane + 2048 * c < H)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xv[t][c][i] = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(t) * H + 32 * lane + 2048 * c + 8 * i);
   // router rows of this block: r = blockIdx.x + G * i (row E = shared gate weights)
   float4 rw[2][KCG];
-  uint2 rx[KCG];
+  uint2 rx[TM][KCG];
 #pragma unroll
   for (int c = 0; c < KCG; ++c) {
     const int kk = 4 * tid + 2048 * c;
     if (kk < H) {
-      rx[c] = *reinterpret_cast<const uint2*>(a.x + kk);
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        if (t < T) rx[t][c] = *reinterpret_cast<const uint2*>(a.x + static_cast<int64_t>(t) * H + kk);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = blockIdx.x + G * i;
@@ -379,123 +271,168 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
     if (n < H) load_dn<KCD>(a.sdn, 0, Is, n, H, lane, dsh[i]);
   }
 
-  // ---- B: router dot products
+  // ---- B: router dot products, every token against this block's rows
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    float acc = 0.f;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int c = 0; c < KCG; ++c) {
-      const int kk = 4 * tid + 2048 * c;
-      if (kk < H && blockIdx.x + G * i <= E) {
-        acc = __builtin_fmaf(__uint_as_float(rx[c].x << 16), rw[i][c].x, acc);
-        acc = __builtin_fmaf(__uint_as_float(rx[c].x & 0xFFFF0000u), rw[i][c].y, acc);
-        acc = __builtin_fmaf(__uint_as_float(rx[c].y << 16), rw[i][c].z, acc);
-        acc = __builtin_fmaf(__uint_as_float(rx[c].y & 0xFFFF0000u), rw[i][c].w, acc);
+    for (int t = 0; t < TM; ++t) {
+      if (t >= T) continue;
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < KCG; ++c) {
+        const int kk = 4 * tid + 2048 * c;
+        if (kk < H && blockIdx.x + G * i <= E) {
+          acc = __builtin_fmaf(__uint_as_float(rx[t][c].x << 16), rw[i][c].x, acc);
+          acc = __builtin_fmaf(__uint_as_float(rx[t][c].x & 0xFFFF0000u), rw[i][c].y, acc);
+          acc = __builtin_fmaf(__uint_as_float(rx[t][c].y << 16), rw[i][c].z, acc);
+          acc = __builtin_fmaf(__uint_as_float(rx[t][c].y & 0xFFFF0000u), rw[i][c].w, acc);
+        }
       }
+      acc = wave_sum(acc);
+      if (lane == 0) red[i][t][wv] = acc;
     }
-    acc = wave_sum(acc);
-    if (lane == 0) red[i][wv] = acc;
-  }
   __syncthreads();
-  if (tid < 2) {
-    const int r = blockIdx.x + G * tid;
+  if (tid < 2 * T) {
+    const int i = tid / T, t = tid - i * T;
+    const int r = blockIdx.x + G * i;
     if (r <= E) {
       float l = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) l += red[tid][w];
+      for (int w = 0; w < kDecWaves; ++w) l += red[i][t][w];
       if (r < E && a.router_bias) l += a.router_bias[r];
-      put(lw + r, tagged(tag, __float_as_uint(l)));
+      put(lw + t * (E + 1) + r, tagged(tag, __float_as_uint(l)));
     }
   }
 
-  // ---- C: shared expert column pair
+  // ---- C: shared expert column pair, every token
   if (has_sh) {
-    const uint32_t hv = swiglu_pair<KCG>(sh, xv, H, lane);
-    if (lane == 0) put(hw + static_cast<int64_t>(k) * hp + p_sh, tagged(tag, hv));
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+      if (t < T) {
+        const uint32_t hv = swiglu_pair<KCG>(sh, xv[t], H, lane);
+        if (lane == 0) put(hw + (static_cast<int64_t>(t) * (k + 1) + k) * hp + p_sh, tagged(tag, hv));
+      }
   }
 
-  // ---- D: routing decision (every block)
-  poll_words<1, 1>(lw, E + 1, tag, s_l, &sy->timeout, [](int) { return true; },
-                                                     s_done);
-  topk_block(s_l, E, k, s_key, s_cand, s_part, s_e, s_v);
+  // ---- D: routing decision of every token (every block)
+  poll_words<(TM * (kDecMaxE + 1) + kDecThreads - 1) / kDecThreads, (TM * (kDecMaxE + 1) + kDecThreads - 1) / kDecThreads>(
+      lw, T * (E + 1), tag, &s_l[0][0], &sy->timeout, [](int) { return true; }, s_done);
+  if constexpr (TM > 1) {
+    // the polled words are [T][E + 1]; the rows of s_l are kDecMaxE + 1 apart
+    for (int t = T - 1; t > 0; --t) {
+      uint32_t v = 0;
+      if (tid <= E) v = (&s_l[0][0])[t * (E + 1) + tid];
+      __syncthreads();
+      if (tid <= E) s_l[t][tid] = v;
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+    if (t < T) topk_block(s_l[t], E, k, s_key, s_cand, s_part, s_e[t], s_v[t]);
   // renormalised weights exp(l_r - l_0) / sum_r' exp(l_r' - l_0), the sum in
   // slot order: lane r takes slot r's exponential.  Every wave computes them
-  // (the same values) into its own row of s_w, so no further barrier is
+  // (the same values) into its own rows of s_w, so no further barrier is
   // needed; [k] = shared gate
-  float* sw = s_w[wv];
-  {
-    const float ex = lane < k ? expf(s_v[lane] - s_v[0]) : 0.f;
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t >= T) continue;
+    float* sw = s_w[wv][t];
+    const float ex = lane < k ? expf(s_v[t][lane] - s_v[t][0]) : 0.f;
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < kDecMaxK; ++r)
       if (r < k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), r));
     const float inv = 1.0f / sum;
     if (lane < k) sw[lane] = ex * inv;
-    if (lane == 0) sw[k] = sigmoidf_(__uint_as_float(s_l[E]));
+    if (lane == 0) sw[k] = sigmoidf_(__uint_as_float(s_l[t][E]));
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's s_w row is written
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's s_w rows are written
   __builtin_amdgcn_wave_barrier();
   if (blockIdx.x == 0) {
-    for (int i = tid; i < E; i += kDecThreads) a.logits[i] = __uint_as_float(s_l[i]);
-    if (tid == 0) a.s_logit[0] = __uint_as_float(s_l[E]);
-    if (tid < k) {
-      a.ids[tid] = s_e[tid];
-      a.wts[tid] = sw[tid];
+    for (int t = 0; t < T; ++t) {
+      for (int i = tid; i < E; i += kDecThreads) a.logits[t * E + i] = __uint_as_float(s_l[t][i]);
+      if (tid == 0) a.s_logit[t] = __uint_as_float(s_l[t][E]);
+      if (tid < k) {
+        a.ids[t * k + tid] = s_e[t][tid];
+        a.wts[t * k + tid] = s_w[0][t][tid];
+      }
+      if (tid == 0) a.gate[t] = s_w[0][t][k];
     }
-    if (tid == 0) a.gate[0] = sw[k];
   }
 
-  // ---- E + F: routed gate/up column pairs, task q = slot * (I/2) + pair.
-  // With hidden <= 2048 this wave's routed down rows are requested right after
-  // its first gate/up rows, so they arrive while h is being produced and
-  // handed over (wider rows leave no registers for that: there they follow
-  // the gate/up work).
+  // ---- E + F: routed gate/up column pairs, task q = (token * k + slot) * (I/2)
+  // + pair.  With hidden <= 2048 this wave's routed down rows are requested
+  // right after its first gate/up rows, so they arrive while h is being
+  // produced and handed over (wider rows leave no registers for that: there
+  // they follow the gate/up work).
   const int ip = I / 2;
-  const int n_tasks = k * ip;
-  DnRow<KCD> dr[kRowsMax][KMAX];
+  const int n_tasks = T * k * ip;
+  DnRow<KCD> dr[kRowsMax][TM * KMAX];
   auto load_down = [&]() {
 #pragma unroll
     for (int i = 0; i < kRowsMax; ++i) {
       const int n = gw + NW * i;
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (n < H && j < k) load_dn<KCD>(a.dn, s_e[j], I, n, H, lane, dr[i][j]);
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (n < H && t < T && j < k) load_dn<KCD>(a.dn, s_e[t][j], I, n, H, lane, dr[i][t * KMAX + j]);
     }
   };
   bool down_issued = false;
   for (int q0 = gw; q0 < n_tasks; q0 += NW * kDecTasks<KCG>) {
     GuPair<KCG> ru[kDecTasks<KCG>];
+    uint4 xq[TM == 1 ? 1 : kDecTasks<KCG>][KCG][4];   // the task's token (one token: xv)
 #pragma unroll
-    for (int t = 0; t < kDecTasks<KCG>; ++t) {
-      const int q = q0 + NW * t;
-      if (q < n_tasks) load_gu<KCG>(a.gu, s_e[q / ip], I, q % ip, H, lane, ru[t]);
+    for (int u = 0; u < kDecTasks<KCG>; ++u) {
+      const int q = q0 + NW * u;
+      if (q < n_tasks) {
+        const int slot = q / ip, t = slot / k;
+        load_gu<KCG>(a.gu, s_e[t][slot - t * k], I, q % ip, H, lane, ru[u]);
+        if constexpr (TM > 1) {
+#pragma unroll
+          for (int c = 0; c < KCG; ++c)
+            if (32 * lane + 2048 * c < H)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                xq[u][c][i] =
+                    *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(t) * H + 32 * lane + 2048 * c + 8 * i);
+        }
+      }
     }
     if (KCG == 1 && !down_issued) {
       load_down();
       down_issued = true;
     }
 #pragma unroll
-    for (int t = 0; t < kDecTasks<KCG>; ++t) {
-      const int q = q0 + NW * t;
+    for (int u = 0; u < kDecTasks<KCG>; ++u) {
+      const int q = q0 + NW * u;
       if (q < n_tasks) {
-        const uint32_t hv = swiglu_pair<KCG>(ru[t], xv, H, lane);
-        if (lane == 0) put(hw + static_cast<int64_t>(q / ip) * hp + q % ip, tagged(tag, hv));
+        const int slot = q / ip, t = slot / k;
+        uint32_t hv;
+        if constexpr (TM == 1)
+          hv = swiglu_pair<KCG>(ru[u], xv[0], H, lane);
+        else
+          hv = swiglu_pair<KCG>(ru[u], xq[u], H, lane);
+        if (lane == 0) put(hw + (static_cast<int64_t>(slot) + t) * hp + q % ip, tagged(tag, hv));
       }
     }
   }
   if (!down_issued) load_down();
 
-  // ---- G: all of h, then down GEMV and combine
-  constexpr int kHWords = (KMAX + 1) * 256 * KCD;   // k + 1 slots of at most 512 KCD columns
+  // ---- G: all of h, then down GEMV and combine, every token
+  constexpr int kHWords = TM * (KMAX + 1) * 256 * KCD;   // T (k + 1) slots of at most 512 KCD columns
   constexpr int kHPerThread = (kHWords + kDecThreads - 1) / kDecThreads;
   // (the widest form, k > 8 with hidden and inter both past 2048 / 512, has no
   // registers to spare: there one word is requested at a time)
   constexpr int kHChunk = KCG * KCD == 4 && KMAX > 8 ? 1 : (kHPerThread < 9 ? kHPerThread : 9);
   poll_words<kHPerThread, kHChunk>(
-      hw, (k + 1) * hp, tag, hs32, &sy->timeout,
+      hw, T * (k + 1) * hp, tag, hs32, &sy->timeout,
       [&](int i) {
-        const int j = i / hp;
-        return i - j * hp < (j < k ? ip : Is / 2);
+        const int slot = i / hp;
+        const int j = slot % (k + 1);
+        return i - slot * hp < (j < k ? ip : Is / 2);
       },
       s_done);
   const uint16_t* hs = reinterpret_cast<const uint16_t*>(hs32);
@@ -503,13 +440,19 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
   for (int i = 0; i < kRowsMax; ++i) {
     const int n = gw + NW * i;
     if (n < H) {
-      float yv = 0.f;
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (j < k) yv = __builtin_fmaf(sw[j], dot_dn<KCD>(dr[i][j], hs + j * a.ldh, I, lane), yv);
-      yv = __builtin_fmaf(sw[k], dot_dn<KCD>(dsh[i], hs + k * a.ldh, Is, lane), yv);
-      yv = wave_sum(yv);
-      if (lane == 0) a.y[n] = f32_to_bf16_bits(yv);
+      for (int t = 0; t < TM; ++t) {
+        if (t >= T) continue;
+        const float* sw = s_w[wv][t];
+        const uint16_t* ht = hs + static_cast<int64_t>(t) * (k + 1) * a.ldh;
+        float yv = 0.f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (j < k) yv = __builtin_fmaf(sw[j], dot_dn<KCD>(dr[i][t * KMAX + j], ht + j * a.ldh, I, lane), yv);
+        yv = __builtin_fmaf(sw[k], dot_dn<KCD>(dsh[i], ht + k * a.ldh, Is, lane), yv);
+        yv = wave_sum(yv);
+        if (lane == 0) a.y[static_cast<int64_t>(t) * H + n] = f32_to_bf16_bits(yv);
+      }
     }
   }
 
@@ -517,24 +460,27 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
   if (tid == 0) put(&sy->gen[blockIdx.x], tag);
 }
 
-bool decode_supported(const moe_dims& d) {
-  return d.hidden <= 2 * 2048 && d.inter <= 2 * 512 && d.shared_inter <= 2 * 512 && d.top_k <= kDecMaxK;
+bool decode_supported(const moe_dims& d, int T) {
+  if (T == 1)
+    return d.hidden <= 2 * 2048 && d.inter <= 2 * 512 && d.shared_inter <= 2 * 512 && d.top_k <= kDecMaxK;
+  return T >= 2 && T <= kDecMaxT && d.hidden <= 2048 && d.inter <= 512 && d.shared_inter <= 512 && d.top_k <= 8;
 }
 
 size_t decode_sync_bytes(const moe_dims& d) {
   const size_t ldh = static_cast<size_t>(div_up(max(d.inter, d.shared_inter), 8) * 8);
-  return offsetof(DecSync, words) + 8 * (static_cast<size_t>(d.n_experts) + 1 + (d.top_k + 1) * ldh / 2);
+  const size_t T = kDecMaxT;
+  return offsetof(DecSync, words) + 8 * T * (static_cast<size_t>(d.n_experts) + 1 + (d.top_k + 1) * ldh / 2);
 }
 
 template <int KCG, int KCD>
 static void launch_dec(const DecArgs& a, size_t shbytes, hipStream_t s) {
   if (a.k <= 8)
-    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, 8>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
+    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, 8, 1>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
   else
-    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, kDecMaxK>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
+    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, kDecMaxK, 1>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
 }
 
-hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y,
+hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, int T, uint16_t* y,
                                const DecodePtrs& p, hipStream_t s) {
   DecArgs a{};
   a.gu = L.gate_up;
@@ -549,6 +495,7 @@ hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint
   a.Is = d.shared_inter;
   a.E = d.n_experts;
   a.k = d.top_k;
+  a.T = T;
   a.x = x;
   a.logits = p.logits;
   a.s_logit = p.s_logit;
@@ -558,9 +505,13 @@ hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint
   a.ldh = static_cast<int>(div_up(max(d.inter, d.shared_inter), 8) * 8);
   a.y = y;
   a.sync = reinterpret_cast<DecSync*>(p.sync);
+  const size_t sh = static_cast<size_t>(T) * (d.top_k + 1) * a.ldh * 2;   // h of all slots in LDS
+  if (T > 1) {   // decode_supported(): hidden <= 2048, inter and shared_inter <= 512, k <= 8
+    hipLaunchKernelGGL((k_decode_layer<1, 1, 8, kDecMaxT>), dim3(kDecBlocks), dim3(kDecThreads), sh, s, a);
+    return hipGetLastError();
+  }
   const int kcg = static_cast<int>(div_up(d.hidden, 2048));
   const int kcd = static_cast<int>(div_up(max(d.inter, d.shared_inter), 512));
-  const size_t sh = static_cast<size_t>(d.top_k + 1) * a.ldh * 2;   // h of all slots in LDS
   switch (kcg * 10 + kcd) {   // decode_supported(): both 1 or 2
     case 11: launch_dec<1, 1>(a, sh, s); break;
     case 12: launch_dec<1, 2>(a, sh, s); break;

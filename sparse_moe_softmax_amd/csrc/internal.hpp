@@ -334,10 +334,12 @@ struct DecodePtrs {
   float* gate;
   void* sync;        // decode_sync_bytes(), zero before the first call on it
 };
-// The whole T == 1 layer as one launch (router, top-k, experts, combine).
-hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, uint16_t* y,
+// The whole layer for 1 <= T <= kDecMaxT tokens as one launch (router, top-k,
+// experts, combine), where decode_supported(d, T).
+constexpr int kDecMaxT = 4;
+hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, int T, uint16_t* y,
                                const DecodePtrs& p, hipStream_t s);
-bool decode_supported(const moe_dims& d);
+bool decode_supported(const moe_dims& d, int T);
 size_t decode_sync_bytes(const moe_dims& d);
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }

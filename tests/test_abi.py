@@ -100,15 +100,24 @@ def test_forward_workspace_checked(m):
     assert L.moe_forward(d, ctypes.byref(layer), FAKE, 4096, FAKE, None, None, None, None, need, None) == -3
     nolayer = m._Layer(q, q, q, q, FAKE, None, None, FAKE)
     assert L.moe_forward(d, ctypes.byref(nolayer), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
+    # the grouped path (T > 4) needs the bf16 router planes; the fused path (T <= 4) the fp32 router
     nor3 = m._Layer(q, q, q, q, FAKE, None, FAKE, None)
-    assert L.moe_forward(d, ctypes.byref(nor3), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
+    assert L.moe_forward(d, ctypes.byref(nor3), FAKE, 64, FAKE, None, None, None, FAKE, need, None) == -1
+    assert "router_w3" in L.moe_last_error_message().decode()
+    norw = m._Layer(q, q, q, q, None, None, FAKE, FAKE)
+    for T in (1, 4):
+        assert L.moe_forward(d, ctypes.byref(norw), FAKE, T, FAKE, None, None, None, FAKE, need, None) == -1
+        assert "router_w is NULL" in L.moe_last_error_message().decode()
+    # the grouped GEMMs (T > 4) read the packed weights
     unpacked = m._Q4(FAKE, FAKE, FAKE, None)
     nopack = m._Layer(unpacked, q, q, q, FAKE, None, FAKE, FAKE)
-    assert L.moe_forward(d, ctypes.byref(nopack), FAKE, 4, FAKE, None, None, None, FAKE, need, None) == -1
+    assert L.moe_forward(d, ctypes.byref(nopack), FAKE, 64, FAKE, None, None, None, FAKE, need, None) == -1
     assert "moe_prepack_q4" in L.moe_last_error_message().decode()
-    # the T == 1 path reads only the canonical arrays
+    # the fused path (1 <= T <= 4) reads only the canonical arrays
     nocanon = m._Layer(m._Q4(None, None, None, FAKE), q, q, q, FAKE, None, FAKE, FAKE)
-    assert L.moe_forward(d, ctypes.byref(nocanon), FAKE, 1, FAKE, None, None, None, FAKE, need, None) == -1
+    for T in (1, 4):
+        assert L.moe_forward(d, ctypes.byref(nocanon), FAKE, T, FAKE, None, None, None, FAKE, need, None) == -1
+        assert "NULL weight pointer" in L.moe_last_error_message().decode()
 
 
 def test_packed_sizes_and_checks(m):

@@ -442,7 +442,7 @@ def test_forward_router_ties(T):
     say("ids of token 0", list(r["ids"][0]), "ties", first, sorted([a8, eighth, b8]))
 
 
-@pytest.mark.parametrize("T,cfg", [(2, None), (512, "t512"), (700, None), (4096, "skew16k")])
+@pytest.mark.parametrize("T,cfg", [(5, None), (512, "t512"), (700, None), (4096, "skew16k")])
 def test_forward_host_routing_equals_forward(T, cfg):
     """The variant that takes the expert counts through the host builds the same
     offsets and block map there (pinned against the oracle on the CPU), so every
