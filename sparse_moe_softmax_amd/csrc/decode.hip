@@ -139,6 +139,7 @@ constexpr int kDecMaxK = 16;
 constexpr int kDecMaxE = 256;
 static_assert(kDecMaxE + 1 <= kDecThreads, "one logit word per thread");
 static_assert(kDecMaxE == 32 * kDecWaves, "top-k stage 1 gives each wave 32 experts");
+static_assert(kDecMaxT <= kDecWaves, "several tokens: one wave per token's top-k");
 
 // Top-k (k <= 16) of the E <= 256 logits (fp32 bits in l[]) by the whole
 // block, in the order larger logit first, then lower expert index (-0 and +0
@@ -327,25 +328,48 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
       __syncthreads();
     }
   }
-#pragma unroll
-  for (int t = 0; t < TM; ++t)
-    if (t < T) topk_block(s_l[t], E, k, s_key, s_cand, s_part, s_e[t], s_v[t]);
   // renormalised weights exp(l_r - l_0) / sum_r' exp(l_r' - l_0), the sum in
-  // slot order: lane r takes slot r's exponential.  Every wave computes them
-  // (the same values) into its own rows of s_w, so no further barrier is
-  // needed; [k] = shared gate
+  // slot order: lane t k + r takes token t's slot r exponential.  Every wave
+  // computes them (the same values) into its own rows of s_w, so no further
+  // barrier is needed; [k] = shared gate
+  if constexpr (TM == 1) {
+    topk_block(s_l[0], E, k, s_key, s_cand, s_part, s_e[0], s_v[0]);
+  } else {
+    // several tokens: wave t takes token t's top-k on its own (eight rounds of
+    // a wave-wide maximum, the same order), all tokens at once
+    if (wv < T) {
+      float v[4];
 #pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    if (t >= T) continue;
-    float* sw = s_w[wv][t];
-    const float ex = lane < k ? expf(s_v[t][lane] - s_v[t][0]) : 0.f;
-    float sum = 0.f;
+      for (int i = 0; i < 4; ++i) v[i] = lane + 64 * i < E ? __uint_as_float(s_l[wv][lane + 64 * i]) : 0.f;
+      int te[16];
+      float tv[16];
+      topk_wave64_regs(v, E, k, te, tv);
 #pragma unroll
-    for (int r = 0; r < kDecMaxK; ++r)
-      if (r < k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), r));
-    const float inv = 1.0f / sum;
-    if (lane < k) sw[lane] = ex * inv;
-    if (lane == 0) sw[k] = sigmoidf_(__uint_as_float(s_l[t][E]));
+      for (int r = 0; r < 8; ++r)
+        if (lane == r && r < k) {
+          s_e[wv][r] = te[r];
+          s_v[wv][r] = tv[r];
+        }
+    }
+    __syncthreads();
+  }
+  {
+    const int tl = min(lane / k, TM - 1), rl = lane - tl * k;   // (lanes past T k hold nothing)
+    const bool mine = lane < T * k;
+    const float ex = mine ? expf(s_v[tl][rl] - s_v[tl][0]) : 0.f;
+    float inv = 0.f;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t >= T) continue;
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < kDecMaxK; ++r)
+        if (r < k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), t * k + r));
+      const float it = 1.0f / sum;
+      if (tl == t) inv = it;
+    }
+    if (mine) s_w[wv][tl][rl] = ex * inv;
+    if (lane < T) s_w[wv][lane][k] = sigmoidf_(__uint_as_float(s_l[lane][E]));
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's s_w rows are written
   __builtin_amdgcn_wave_barrier();

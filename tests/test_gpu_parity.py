@@ -386,29 +386,31 @@ def test_decode_forms(hidden, inter, shared, E, k):
 
 
 def test_decode_handover_words():
-    """The fused T == 1 layer passes logits and h between its workgroups in
-    tagged words at the start of the workspace: after n calls every block has
-    recorded n completed calls, no wait timed out, and repeated calls on one
-    workspace give identical outputs."""
+    """The fused layer passes logits and h between its workgroups in tagged
+    words at the start of the workspace: after n calls (one-token and
+    three-token calls alternating) every block has recorded n completed calls,
+    no wait timed out, and repeated calls on one workspace give identical
+    outputs."""
     say("decode hand-over words")
     m = gu.moe()
     c = synth.CONFIGS["decode"]
     md = gu.to_dims(c.dims)
     dl = gu.device_layer(synth.make_layer(c.dims, c.seed, layer=3), c.dims)
-    ws = m.moe_workspace(md, 1)
     outs = []
+    ws = m.moe_workspace(md, 4)
     for step in range(6):
-        x = synth.activations(1, c.dims.hidden, c.seed, step=step % 2).cuda()
+        # one token and three tokens (the multi-token form) alternate on one workspace
+        T = 1 if step % 2 == 0 else 3
+        x = synth.activations(T, c.dims.hidden, c.seed, step=step % 4).cuda()
         outs.append(m.moe_forward(md, dl, x, workspace=ws).clone())
         torch.cuda.synchronize()
         words = ws[:1028].view(torch.int32).cpu()
         assert torch.all(words[:256] == step + 1)      # calls completed, per block
         assert int(words[256]) == 0                     # timeout word
-    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[0], outs[4])
-    assert torch.equal(outs[1], outs[3]) and torch.equal(outs[1], outs[5])
+    assert torch.equal(outs[0], outs[4]) and torch.equal(outs[1], outs[5])
 
 
-@pytest.mark.parametrize("T", [1, 5, 300])
+@pytest.mark.parametrize("T", [1, 3, 5, 300])
 def test_forward_router_ties(T):
     """Duplicated router rows give bitwise-equal logits: for token 0 the top
     expert's row is copied to a lower and a higher expert index (a three-way tie
