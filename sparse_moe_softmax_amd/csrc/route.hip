@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_router_gemm(const uint16_t* __restrict_
 // outputs as in the 64 x 64 form.
 constexpr int kRwM = 128;
 constexpr int kRwN = 128;
-constexpr int kRwStages = 4;
+constexpr int kRwStages = 2;   // 66 KB: two workgroups per CU, as for the 64 x 64 form
 constexpr int kRwX = kRwM * 64;                   // x tile: 128 rows x 32 K
 constexpr int kRwW = 3 * kRwN * 64;               // weight planes
 constexpr int kRwS = 4 * 256;                     // shared-gate weights (one copy per wave)
@@ -311,8 +311,8 @@ __global__ __launch_bounds__(256) void k_router_gemm_wide(const uint16_t* __rest
   }
 }
 
-// Tile form and K splits for T tokens: the wide form, unsplit, where its tiles
-// alone fill the chip (256 workgroups); else 64 x 64 tiles, split over K as
+// Tile form and K splits for T tokens: the wide form where its tiles alone
+// fill the chip (256 workgroups), else 64 x 64 tiles; either split over K as
 // far as needed (at most kMaxSplits) to give every CU two workgroups.
 struct RouterPlan {
   bool wide;
@@ -320,7 +320,11 @@ struct RouterPlan {
 };
 static RouterPlan router_plan(int T, int H, int E) {
   const int64_t wide_tiles = div_up(T, kRwM) * div_up(E, kRwN);
-  if (wide_tiles >= 256) return {true, 1};
+  if (wide_tiles >= 256) {
+    int ws = static_cast<int>(div_up(512, wide_tiles));
+    while (ws > 1 && (H / 32) % ws) --ws;
+    return {true, ws};
+  }
   const int64_t tiles = div_up(T, kRtM) * div_up(E, kRtN);
   const int kg = H / 64;
   int want = static_cast<int>(div_up(512, tiles));
