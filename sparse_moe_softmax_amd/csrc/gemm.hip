@@ -649,10 +649,15 @@ hipError_t launch_prepack_q4(const moe_dims& d, int matrix, const moe_q4& w, int
 
 // out[t][n] = bf16( sum_{j<k} w[t][j] * slot[t][j][n] + gate[t] * slot[t][k][n] ),
 // slots fp16, summed in fp32 in slot order (shared expert last); w or gate
-// NULL = weights of 1 (slots already weighted).  8 columns per thread.
+// NULL = weights of 1 (slots already weighted).  8 columns per thread.  With
+// k known at compile time (K > 0) all k + 1 slot vectors are requested before
+// the sum, so a thread waits for one memory round trip, not k + 1; K = 0 takes
+// k at run time.
+template <int K>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ slots, const float* __restrict__ w,
                                                  const float* __restrict__ gate, uint16_t* __restrict__ out, int T,
-                                                 int H, int k) {
+                                                 int H, int k_rt) {
+  const int k = K > 0 ? K : k_rt;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // 8-column group
   const int per_tok = H / 8;
   if (i >= static_cast<int64_t>(T) * per_tok) return;
@@ -660,15 +665,29 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
   const int c8 = static_cast<int>(i % per_tok) * 8;
   const uint16_t* src = slots + t * (k + 1) * H + c8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j <= k; ++j) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
+  auto add = [&](const uint4& v, float wj) {
     const f16x2 p[4] = {__builtin_bit_cast(f16x2, v.x), __builtin_bit_cast(f16x2, v.y),
                         __builtin_bit_cast(f16x2, v.z), __builtin_bit_cast(f16x2, v.w)};
-    const float wj = j == k ? (gate ? gate[t] : 1.0f) : (w ? w[t * k + j] : 1.0f);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       acc[2 * u] = __builtin_fmaf(wj, static_cast<float>(p[u].x), acc[2 * u]);
       acc[2 * u + 1] = __builtin_fmaf(wj, static_cast<float>(p[u].y), acc[2 * u + 1]);
+    }
+  };
+  if constexpr (K > 0) {
+    uint4 v[K + 1];
+#pragma unroll
+    for (int j = 0; j <= K; ++j) v[j] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
+    float wj[K + 1];
+#pragma unroll
+    for (int j = 0; j < K; ++j) wj[j] = w ? w[t * K + j] : 1.0f;
+    wj[K] = gate ? gate[t] : 1.0f;
+#pragma unroll
+    for (int j = 0; j <= K; ++j) add(v[j], wj[j]);
+  } else {
+    for (int j = 0; j <= k; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
+      add(v, j == k ? (gate ? gate[t] : 1.0f) : (w ? w[t * k + j] : 1.0f));
     }
   }
   uint4 o;
@@ -682,8 +701,11 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
 hipError_t launch_combine(const uint16_t* slots, const float* w, const float* gate, uint16_t* out, int T, int H, int k,
                           hipStream_t s) {
   const int64_t n = static_cast<int64_t>(T) * (H / 8);
-  hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>(div_up(n, 256))), dim3(256), 0, s, slots, w, gate, out, T,
-                     H, k);
+  const dim3 grid(static_cast<unsigned>(div_up(n, 256)));
+  if (k == 8)
+    hipLaunchKernelGGL(k_combine<8>, grid, dim3(256), 0, s, slots, w, gate, out, T, H, k);
+  else
+    hipLaunchKernelGGL(k_combine<0>, grid, dim3(256), 0, s, slots, w, gate, out, T, H, k);
   return hipGetLastError();
 }
 
