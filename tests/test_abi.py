@@ -195,8 +195,9 @@ def test_host_routing_checks(m):
     hb = (ctypes.c_uint8 * need)()
     q = m._Q4(FAKE, FAKE, FAKE, FAKE)
     layer = m._Layer(q, q, q, q, FAKE, None, FAKE, FAKE)
-    # T == 1 is not covered; a short host buffer is refused before any launch
-    assert L.moe_forward_host_routing(d, ctypes.byref(layer), FAKE, 1, FAKE, None, None, FAKE, 1 << 30, vp(hb), need,
-                                      None) == -2
+    # the fused sizes (1 <= T <= 4 here) are not covered; a short host buffer is refused before any launch
+    for T in (1, 3, 4):
+        assert L.moe_forward_host_routing(d, ctypes.byref(layer), FAKE, T, FAKE, None, None, FAKE, 1 << 30, vp(hb),
+                                          need, None) == -2
     assert L.moe_forward_host_routing(d, ctypes.byref(layer), FAKE, 512, FAKE, None, None, FAKE, 1 << 30, vp(hb),
                                       need - 4, None) == -1

@@ -416,7 +416,8 @@ def test_forward_router_ties(T):
     expert's row is copied to a lower and a higher expert index (a three-way tie
     for first place, which pushes the old 6th expert to 8th place) and that
     expert's row to two others (a three-way tie across the cut).  The GPU ids must be the oracle's top-k of the GPU logits: lower expert
-    index first among equal logits, on the decode (T == 1) and prefill paths."""
+    index first among equal logits, on the fused (T = 1, 3) and grouped (T = 5,
+    300) paths."""
     say("forward router ties T", T)
     d = MODEL
     lay = synth.make_layer(d, 501 + T)
