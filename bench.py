@@ -11,8 +11,8 @@ weights).  Also reported: the layer's fraction of dense bf16 MFMA peak, the
 dominant kernel's roofline (timed live with HIP events on the launch stream),
 per-stage times, batch-1 decode over 40 stacked layers x 256 steps as HBM GB/s,
 the GPU-resident vs host-synchronised routing ablation at T=512, a T=1..16
-small-batch sweep, and the CPU oracle timed on a bounded token sample of the
-same workload.
+small-batch sweep, T=64 and T=512 as fractions of HBM bandwidth, and the CPU
+oracle timed on a bounded token sample of the same workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -236,10 +236,11 @@ def bench_routing_ablation(cfg, steps, warmup):
             "outputs_bitwise_equal": same, "timing": f"eager launches, wall clock, mean of {steps} layers"}
 
 
-def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20):
-    """Decode-like small batches: one pass over n_layers distinct layers per
-    replay (a HIP graph), algorithmic bytes = the experts the tokens touch +
-    shared expert + router + activations, per layer."""
+def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20, seeds=None):
+    """Memory-bound batch sizes: one pass of T tokens over n_layers distinct
+    layers per replay (a HIP graph), algorithmic bytes = the experts the tokens
+    touch + shared expert + router + activations, per layer.  seeds: per-T
+    activation seeds (default: the configuration's seed, step T)."""
     import numpy as np
     import torch
     import sparse_moe_softmax_amd as moe
@@ -250,7 +251,7 @@ def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20):
     eb, sb = expert_bytes(d), expert_bytes(synth_dims_shared(d))
     out = []
     for T in Ts:
-        x = synth.activations(T, d.hidden, cfg.seed, step=T).cuda()
+        x = synth.activations(T, d.hidden, seeds[T] if seeds else cfg.seed, step=0 if seeds else T).cuda()
         ws = moe.moe_workspace(md, T)
         ys = torch.empty((n_layers, T, d.hidden), dtype=torch.bfloat16, device="cuda")
         ids = torch.empty((n_layers, T, d.top_k), dtype=torch.int32, device="cuda")
@@ -282,7 +283,8 @@ def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20):
                     "bytes_per_layer": int(bytes_layer), "GBs": round(gbs, 1),
                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                     "path": "fused layer, one launch" if T <= 4 else "router GEMM, grouping, grouped GEMMs"})
-        log(f"small T={T}: {us_layer:.2f} us/layer, {out[-1]['experts_touched']} experts, {gbs:.0f} GB/s")
+        log(f"T={T}: {us_layer:.2f} us/layer, {out[-1]['experts_touched']} experts, {gbs:.0f} GB/s "
+            f"({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM)")
     return {"layers": n_layers, "launch": f"HIP graph of one pass over {n_layers} layers, {reps} replays",
             "points": out}
 
@@ -459,6 +461,10 @@ def main():
     if not args.no_extras:
         out["routing_ablation"] = bench_routing_ablation(synth.CONFIGS["t512"], max(20, args.steps), args.warmup)
         out["small_t"] = bench_small_t(synth.CONFIGS["decode"])
+        # the memory-bound prefill sizes (64 and 512 tokens, one layer each in
+        # its own configuration) on the same footing: algorithmic bytes / time
+        mid = {c.T: c.seed for c in (synth.CONFIGS["t64"], synth.CONFIGS["t512"])}
+        out["hbm_bound_prefill"] = bench_small_t(synth.CONFIGS["t512"], Ts=tuple(sorted(mid)), seeds=mid)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"], out["parity_sample"] = cpu_baseline(res, args.cpu_sample, threads)
