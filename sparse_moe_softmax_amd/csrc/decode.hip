@@ -88,10 +88,10 @@ __device__ inline uint64_t tagged(uint32_t tag, uint32_t payload) {
 // carried `tag`.  Thread t owns words t + kDecThreads * m, m < M: it requests
 // its pending words together, up to C at a time (so at most C owned words cost
 // one memory round trip per round), and a word once seen with the tag is not
-// requested again.  The block agrees
-// on "all done" with one barrier per round: wave w writes its verdict to
-// done[round & 1][w] (a wave cannot reach round r + 2's write before every wave
-// has passed round r + 1's barrier, that is, has read round r's verdicts).
+// requested again.  The block agrees on "all done" with one barrier per round:
+// wave w writes its verdict to done[round & 1][w] (a wave cannot reach round
+// r + 2's write before every wave has passed round r + 1's barrier, that is,
+// has read round r's verdicts).
 template <int M, int C, class Live>
 __device__ inline void poll_words(const uint64_t* words, int n, uint32_t tag, uint32_t* out, uint32_t* timeout,
                                   Live live, uint32_t (&done)[2][kDecWaves]) {
@@ -137,7 +137,7 @@ template <int KCG>
 constexpr int kDecTasks = KCG == 1 ? 2 : 1;
 constexpr int kDecMaxK = 16;
 constexpr int kDecMaxE = 256;
-static_assert(kDecMaxE + 1 <= kDecThreads, "one logit word per thread");
+static_assert(kDecMaxE + 1 <= kDecThreads, "one token's logit words: at most one per thread");
 static_assert(kDecMaxE == 32 * kDecWaves, "top-k stage 1 gives each wave 32 experts");
 static_assert(kDecMaxT <= kDecWaves, "several tokens: one wave per token's top-k");
 
