@@ -39,6 +39,7 @@
 // a CU), so every wait ends; a wait that exceeds kSpinLimit polls sets the
 // timeout word and carries on, so a launch always completes.
 #include "gemv.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -341,15 +342,25 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = lane + 64 * i < E ? __uint_as_float(s_l[wv][lane + 64 * i]) : 0.f;
-      int te[16];
-      float tv[16];
-      topk_wave64_regs(v, E, k, te, tv);
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (lane == r && r < k) {
-          s_e[wv][r] = te[r];
-          s_v[wv][r] = tv[r];
+      if (k == 8) {
+        int my_e;
+        float my_v;
+        topk_wave64_fixed<8>(v, E, my_e, my_v);
+        if (lane < 8) {
+          s_e[wv][lane] = my_e;
+          s_v[wv][lane] = my_v;
         }
+      } else {
+        int te[16];
+        float tv[16];
+        topk_wave64_regs(v, E, k, te, tv);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          if (lane == r && r < k) {
+            s_e[wv][r] = te[r];
+            s_v[wv][r] = tv[r];
+          }
+      }
     }
     __syncthreads();
   }
