@@ -73,7 +73,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 
 // Workspace regions of moe_forward.
 struct Ws {
-  size_t sync, logits, s, rparts, sparts, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, ntiles, h, hsh,
+  size_t sync, logits, s, rparts, sparts, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, trows, ntiles, h, hsh,
       slots;
   int splits;
   size_t total;
@@ -107,6 +107,7 @@ Ws layout(const moe_dims& d, int32_t T) {
   w.perm = take(F * 4);
   w.inv = take(F * 4);
   w.bmap = take(mt * 2 * 4);
+  w.trows = take(mt * 4);
   w.ntiles = take(4);
   w.h = take(F * I * 2);
   w.hsh = take(static_cast<size_t>(T) * Is * 2);
@@ -232,7 +233,7 @@ moe_status moe_group(const moe_dims* d, const int32_t* ids, int32_t T, int32_t b
   int32_t* tilebase = at<int32_t>(workspace, align256(ntile * d->n_experts * 4));
   if ((st = hip_check(launch_tile_hist(ids, T, d->top_k, d->n_experts, tilehist, s), "tile histogram"))) return st;
   return hip_check(launch_group(ids, tilehist, tilebase, T, d->top_k, d->n_experts, block_m, counts, offsets, perm,
-                                inv_perm, block_map, max_tiles, n_tiles, s),
+                                inv_perm, block_map, max_tiles, n_tiles, nullptr, s),
                    "grouping");
 }
 
@@ -324,7 +325,8 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   const int E = d->n_experts, k = d->top_k;
   const int mt = moe_max_tiles(T, k, E, kBM);
   // shared-expert chunks of kBM rows go first in the same launches as the routed tiles
-  const GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM))};
+  int32_t* trows = at<int32_t>(workspace, w.trows);
+  const GemmTiles tl{perm, offsets, bmap, ntiles, mt, kBM, static_cast<int32_t>(div_up(T, kBM)), trows};
 
   // router output: final logits (one K split) or per-split partial sums that top-k adds up in order
   const int S = w.splits;
@@ -341,7 +343,7 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
     return st;
   if (run(MOE_STAGE_GROUP) &&
       (st = hip_check(launch_group(ids, tilehist, at<int32_t>(workspace, w.tilebase), T, k, E, kBM, counts, offsets,
-                                   perm, at<int32_t>(workspace, w.inv), bmap, mt, ntiles, s),
+                                   perm, at<int32_t>(workspace, w.inv), bmap, mt, ntiles, trows, s),
                       "grouping")))
     return st;
   if (run(MOE_STAGE_GATE_UP) &&
@@ -440,7 +442,7 @@ moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* L, const
       (st = hip_check(hipMemcpyAsync(ntiles, h_ntiles, 4, hipMemcpyHostToDevice, s), "n_tiles")) ||
       (st = hip_check(launch_group_scatter(ids, counts, tilebase, T, k, E, kBM, offsets,
                                            at<int32_t>(workspace, w.perm), at<int32_t>(workspace, w.inv), bmap, mt,
-                                           ntiles, false, s),
+                                           ntiles, false, at<int32_t>(workspace, w.trows), s),
                       "permutation")))
     return st;
   return moe_forward_stages(d, L, x, T, y, nullptr, ids_out, w_out, workspace, workspace_bytes, MOE_STAGE_GATE_UP,

@@ -88,6 +88,7 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* block_map;
   const int32_t* n_tiles;
+  const int32_t* tile_rows;   // rows per routed tile (NULL: from offsets)
   const float* row_w;   // routed: weight per flat slot
   const float* gate;    // shared: sigmoid gate per token
   int block_m;
@@ -442,7 +443,9 @@ __global__ __launch_bounds__(kGemmThreads, kGemmOcc) void k_gemm_q4(GemmArgs g) 
     t.which = 0;
     e = g.block_map[2 * tile];
     t.row0 = g.block_map[2 * tile + 1];
-    t.rows = min(g.block_m, g.offsets[e + 1] - t.row0);
+    // the tile's height arrives with its block-map entry when the grouping
+    // wrote it, else it follows from the expert's segment end
+    t.rows = g.tile_rows ? g.tile_rows[tile] : min(g.block_m, g.offsets[e + 1] - t.row0);
   }
   t.K = g.K[t.which];
   t.N = g.N[t.which];
@@ -515,6 +518,7 @@ static void fill_common(GemmArgs& g, const moe_dims& d, const GemmTiles& tl, int
   g.offsets = tl.offsets;
   g.block_map = tl.block_map;
   g.n_tiles = tl.n_tiles;
+  g.tile_rows = tl.tile_rows;
   g.block_m = tl.block_m;
   g.n_sh = shared ? tl.n_shared_chunks : 0;
   g.max_tiles = tl.max_tiles;

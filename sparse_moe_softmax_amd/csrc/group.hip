@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
                                                        int block_m, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
                                                        int32_t* __restrict__ block_map, int max_tiles,
-                                                       int32_t* __restrict__ n_tiles, int write_map) {
+                                                       int32_t* __restrict__ n_tiles, int write_map,
+                                                       int32_t* __restrict__ tile_rows) {
   __shared__ int base[256];
   __shared__ int sm[4];
   const int tid = threadIdx.x;
@@ -92,24 +93,30 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
   const int off = block_excl_scan256(c, sm, &total);
   if (tid < E) base[tid] = off + tilebase[static_cast<int64_t>(blockIdx.x) * E + tid];
 
-  if (blockIdx.x == 0 && write_map) {
+  if (blockIdx.x == 0 && (write_map || tile_rows)) {
     const int nt = (c + block_m - 1) / block_m;
     int nt_total;
     const int toff = block_excl_scan256(nt, sm, &nt_total);
-    if (tid < E) {
-      offsets[tid] = off;
-      for (int m = 0; m < nt; ++m) {
-        block_map[2 * (toff + m)] = tid;
-        block_map[2 * (toff + m) + 1] = off + m * block_m;
+    // rows of every tile, so that a GEMM tile learns its height in the same
+    // round trip as its block-map entry
+    if (tile_rows && tid < E)
+      for (int m = 0; m < nt; ++m) tile_rows[toff + m] = min(block_m, c - m * block_m);
+    if (write_map) {
+      if (tid < E) {
+        offsets[tid] = off;
+        for (int m = 0; m < nt; ++m) {
+          block_map[2 * (toff + m)] = tid;
+          block_map[2 * (toff + m) + 1] = off + m * block_m;
+        }
       }
-    }
-    if (tid == 0) {
-      offsets[E] = total;
-      *n_tiles = nt_total;
-    }
-    for (int i = nt_total + tid; i < max_tiles; i += 256) {
-      block_map[2 * i] = -1;
-      block_map[2 * i + 1] = -1;
+      if (tid == 0) {
+        offsets[E] = total;
+        *n_tiles = nt_total;
+      }
+      for (int i = nt_total + tid; i < max_tiles; i += 256) {
+        block_map[2 * i] = -1;
+        block_map[2 * i + 1] = -1;
+      }
     }
   }
   __syncthreads();
@@ -151,20 +158,21 @@ hipError_t launch_group_counts(const int32_t* tilehist, int32_t* tilebase, int T
 
 hipError_t launch_group_scatter(const int32_t* ids, const int32_t* counts, const int32_t* tilebase, int T, int k,
                                 int E, int block_m, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                                int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map, hipStream_t s) {
+                                int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map,
+                                int32_t* tile_rows, hipStream_t s) {
   const int ntile = static_cast<int>(div_up(T, kTopkTile));
   hipLaunchKernelGGL(k_group_scatter, dim3(ntile), dim3(256), 0, s, ids, counts, tilebase, T, k, E, block_m, offsets,
-                     perm, inv_perm, block_map, max_tiles, n_tiles, write_map ? 1 : 0);
+                     perm, inv_perm, block_map, max_tiles, n_tiles, write_map ? 1 : 0, tile_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
                         int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                        int32_t* block_map, int max_tiles, int32_t* n_tiles, hipStream_t s) {
+                        int32_t* block_map, int max_tiles, int32_t* n_tiles, int32_t* tile_rows, hipStream_t s) {
   hipError_t err = launch_group_counts(tilehist, tilebase, T, E, counts, s);
   if (err != hipSuccess) return err;
   return launch_group_scatter(ids, counts, tilebase, T, k, E, block_m, offsets, perm, inv_perm, block_map, max_tiles,
-                              n_tiles, true, s);
+                              n_tiles, true, tile_rows, s);
 }
 
 }  // namespace moe

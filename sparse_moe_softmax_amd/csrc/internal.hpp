@@ -255,6 +255,7 @@ struct GemmTiles {
   int32_t max_tiles;         // routed tile bound (grid sizing)
   int32_t block_m;           // rows per routed tile (<= kBM)
   int32_t n_shared_chunks;   // shared-expert tiles of kBM rows put first (0 = none)
+  const int32_t* tile_rows;  // [max_tiles] rows of each routed tile, or NULL: from offsets
 };
 
 // Geometry of the packed (matrix-core) layout of one expert matrix: slices of
@@ -307,12 +308,14 @@ hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* ti
 // offsets + permutation (+ block map and n_tiles when write_map).
 hipError_t launch_group_counts(const int32_t* tilehist, int32_t* tilebase, int T, int E, int32_t* counts,
                                hipStream_t s);
+// tile_rows (nullable): rows of each tile of the block map, written in either case.
 hipError_t launch_group_scatter(const int32_t* ids, const int32_t* counts, const int32_t* tilebase, int T, int k,
                                 int E, int block_m, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                                int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map, hipStream_t s);
+                                int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map,
+                                int32_t* tile_rows, hipStream_t s);
 hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
                         int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                        int32_t* block_map, int max_tiles, int32_t* n_tiles, hipStream_t s);
+                        int32_t* block_map, int max_tiles, int32_t* n_tiles, int32_t* tile_rows, hipStream_t s);
 hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* x,
                               const GemmTiles& tl, int T, uint16_t* h, uint16_t* h_sh, hipStream_t s);
 hipError_t launch_gemm_scatter(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
