@@ -59,12 +59,13 @@ constexpr int kBStage = kSliceRows * 32;         // int4 codes of 256 weight row
 constexpr int kPackBlock = kBStage + kSliceRows * 4;  // + (fp16 scale, fp16 bias) per row = 9216 B
 constexpr int kGemmOcc = 2;                      // workgroups per CU: LDS and registers are split
 constexpr int kRingBytes = (160 * 1024 / kGemmOcc - kBM * 12 - 512) / 256 * 256;  // LDS ring shared by all stages
-// A stage holds the live rows only (MT 32-row sub-tiles, 4 KB each); the
+// A stage holds KS consecutive 64-wide K blocks: per block the live rows only
+// (MT 32-row sub-tiles, 4 KB each) and the slice's packed weight block.  The
 // ring takes as many stages as fit, at most 8 (3 for a 128-row tile).
-template <int MT>
+template <int MT, int KS>
 struct Ring {
-  static constexpr int kA = MT * 32 * 128;
-  static constexpr int kStage = kA + kPackBlock;
+  static constexpr int kA = MT * 32 * 128;          // activation bytes of one K block
+  static constexpr int kStage = KS * (kA + kPackBlock);
   static constexpr int kStages = (kRingBytes / kStage) < 8 ? (kRingBytes / kStage) : 8;
   static_assert(kStages >= 3, "ring too shallow");
 };
@@ -110,7 +111,11 @@ struct Tile {
   const uint8_t* pbase;   // packed blocks of this expert and slice
 };
 
-// K loop + epilogue for a tile of MT 32-row sub-tiles (straight-line code).
+// K loop + epilogue for a tile of MT 32-row sub-tiles (straight-line code),
+// KS K blocks per ring stage.  One-sub-tile tiles (remainder tiles, and every
+// tile of a small batch) take two K blocks per stage when the K blocks pair
+// up: their iteration is dominated by its fixed chain (wait, barrier, load
+// issue, fragment reads), which is then paid once per 128 of K.
 //
 // MFMA v_mfma_f32_32x32x16_bf16.  Within a K block of 64 the lane group
 // g = lane/32 covers K offsets [32g, 32g+32); k-step s (0..3) of a lane holds
@@ -118,14 +123,15 @@ struct Tile {
 // A fragment: row lane%32 of the sub-tile; B fragment: weight row (column)
 // lane%32 of the column group; C: acc[m][c][j] holds row 8(j/4) + 4g + (j%4),
 // column lane%32.
-template <int MODE, int MT>
+template <int MODE, int MT, int KS>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsigned char* ring,
                                           int64_t* s_drow, float* s_wt) {
-  constexpr int kAI = MT;                          // A direct loads per wave per stage (8 rows each)
-  constexpr int kDma = kAI + 3;                   // + 2 code loads + scale/bias
-  constexpr int kStages = Ring<MT>::kStages;
-  constexpr int kStageBytes = Ring<MT>::kStage;
-  constexpr int kAStage = Ring<MT>::kA;
+  constexpr int kAI = MT;                          // A direct loads per wave per K block (8 rows each)
+  constexpr int kDma = KS * (kAI + 3);            // + 2 code loads + scale/bias, per K block
+  constexpr int kStages = Ring<MT, KS>::kStages;
+  constexpr int kStageBytes = Ring<MT, KS>::kStage;
+  constexpr int kAStage = Ring<MT, KS>::kA;        // stage layout: A of each K block, then B of each
+  constexpr int kBOff = KS * kAStage;
   static_assert((kStages - 2) * kDma <= 63, "vmcnt range");
   const int wave = t.wave, lane = t.lane;
   const int col = lane & 31, gq = lane >> 5;
@@ -168,12 +174,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 
   auto issue = [&](int kb) {
     const uint32_t st = ring_s + (kb % kStages) * kStageBytes;
-    const uint32_t aoff = kb * 128, boff = kb * kPackBlock;
 #pragma unroll
-    for (int j = 0; j < kAI; ++j) bdma16(arsrc, asrc[j], aoff, st + (wave_s * kAI + j) * 1024);
+    for (int u = 0; u < KS; ++u) {
+      const uint32_t aoff = (kb * KS + u) * 128, boff = (kb * KS + u) * kPackBlock;
+      const uint32_t sa = st + u * kAStage, sb = st + kBOff + u * kPackBlock;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) bdma16(brsrc, bsrc + j * 1024, boff, st + kAStage + wave_s * 2048 + j * 1024);
-    bdma4(brsrc, ssrc, boff, st + kAStage + kBStage + wave_s * 256);
+      for (int j = 0; j < kAI; ++j) bdma16(arsrc, asrc[j], aoff, sa + (wave_s * kAI + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bdma16(brsrc, bsrc + j * 1024, boff, sb + wave_s * 2048 + j * 1024);
+      bdma4(brsrc, ssrc, boff, sb + kBStage + wave_s * 256);
+    }
   };
 
   f32x16 acc[MT][2];
@@ -184,20 +194,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[m][c][j] = 0.f;
 
-  const int kg = t.kg;
+  const int kg = t.kg / KS;   // ring stages (iterations)
 
   // Codes and dequantisation constants of this wave's two 32-column groups in a stage.
   struct BRaw {
     uint4 codes[2];
     DqConst dc[2];
   };
-  auto read_b = [&](int kb, BRaw& r) {
-    const unsigned char* st = ring + (kb % kStages) * kStageBytes;
+  auto read_b = [&](int kb, int u, BRaw& r) {
+    const unsigned char* sb0 = ring + (kb % kStages) * kStageBytes + kBOff + u * kPackBlock;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int i = wave * 64 + c * 32 + col;
-      r.codes[c] = *reinterpret_cast<const uint4*>(st + kAStage + i * 32 + b_half(i, gq) * 16);
-      const uint32_t sb = *reinterpret_cast<const uint32_t*>(st + kAStage + kBStage + i * 4);
+      r.codes[c] = *reinterpret_cast<const uint4*>(sb0 + i * 32 + b_half(i, gq) * 16);
+      const uint32_t sb = *reinterpret_cast<const uint32_t*>(sb0 + kBStage + i * 4);
       r.dc[c] = dq_const(static_cast<uint16_t>(sb), static_cast<uint16_t>(sb >> 16));
     }
   };
@@ -242,20 +252,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
     __builtin_amdgcn_s_barrier();   // stage kb landed for every wave; stage kb-1 consumed
     if (kSteady || kb + kStages - 1 < kg) issue(kb + kStages - 1);
     const unsigned char* st = ring + (kb % kStages) * kStageBytes;
-    BRaw raw;
-    read_b(kb, raw);
+    BRaw raw[KS];
+#pragma unroll
+    for (int u = 0; u < KS; ++u) read_b(kb, u, raw[u]);
     read_a(st, 0, af[0]);
     bf16x8 bq[2][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) bq[0][c] = dq(raw, c, 0);
+    for (int c = 0; c < 2; ++c) bq[0][c] = dq(raw[0], c, 0);
+    // k-step q of the stage: K block q / 4, k-step q % 4 within it
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) read_a(st, ks + 1, af[(ks + 1) & 1]);
+    for (int q = 0; q < 4 * KS; ++q) {
+      const int nu = (q + 1) >> 2, nks = (q + 1) & 3;
+      if (q + 1 < 4 * KS) read_a(st + nu * kAStage, nks, af[(q + 1) & 1]);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[ks & 1][m], bq[ks & 1][c], acc[m][c]);
-        if (ks < 3) bq[(ks + 1) & 1][c] = dq(raw, c, ks + 1);
+        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[q & 1][m], bq[q & 1][c], acc[m][c]);
+        if (q + 1 < 4 * KS) bq[(q + 1) & 1][c] = dq(raw[nu], c, nks);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -274,7 +287,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
     else if (more)
       wait_stages<kDma, kStages - 3>(min(kStages - 3, kg - 2 - kb));
     BRaw raw;
-    if (more) read_b(kb + 1, raw);   // this wave's own loads: no barrier needed
+    if (more) read_b(kb + 1, 0, raw);   // this wave's own loads: no barrier needed
     __builtin_amdgcn_s_barrier();    // stage kb+1 landed for every wave; stage kb-1 consumed
     if (kSteady || kb + kStages - 1 < kg) issue(kb + kStages - 1);
     const unsigned char* st = ring + (kb % kStages) * kStageBytes;
@@ -304,15 +317,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
   int my_f = 0;
   if (deferred_rows && t.which == 0 && static_cast<int>(threadIdx.x) < t.rows) my_f = g.perm[t.row0 + threadIdx.x];
   const int steady_end = kg - (kStages - 1);   // iterations kb < steady_end are steady
-  if constexpr (MT <= 2) {
-    static_assert(Ring<MT>::kStages >= 3, "the ahead loop waits one stage ahead");
+  if constexpr (MT <= 2 && KS == 1) {
+    static_assert(Ring<MT, KS>::kStages >= 3, "the ahead loop waits one stage ahead");
     // stage 0 landed, dequantised, and its first A fragments read
     wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1));
     __builtin_amdgcn_s_barrier();
     bf16x8 b0[2][4], b1[2][4];
     {
       BRaw raw;
-      read_b(0, raw);
+      read_b(0, 0, raw);
       read_a(ring, 0, af[0]);
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -493,9 +506,15 @@ __global__ __launch_bounds__(kGemmThreads, kGemmOcc) void k_gemm_q4(GemmArgs g) 
   switch ((t.rows + 31) >> 5) {
 #define MOE_MT_CASE(n) \
   case n:              \
-    gemm_tile<MODE, n>(g, t, ring, s_drow, s_wt); \
+    gemm_tile<MODE, n, 1>(g, t, ring, s_drow, s_wt); \
     break;
-    MOE_MT_CASE(1) MOE_MT_CASE(2) MOE_MT_CASE(3)
+    case 1:
+      if ((t.kg & 1) == 0)
+        gemm_tile<MODE, 1, 2>(g, t, ring, s_drow, s_wt);
+      else
+        gemm_tile<MODE, 1, 1>(g, t, ring, s_drow, s_wt);
+      break;
+    MOE_MT_CASE(2) MOE_MT_CASE(3)
 #if MOE_BM > 96
     MOE_MT_CASE(4)
 #endif
