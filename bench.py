@@ -11,8 +11,9 @@ weights).  Also reported: the layer's fraction of dense bf16 MFMA peak, the
 dominant kernel's roofline (timed live with HIP events on the launch stream),
 per-stage times, batch-1 decode over 40 stacked layers x 256 steps as HBM GB/s,
 the GPU-resident vs host-synchronised routing ablation at T=512, a T=1..16
-small-batch sweep, T=64 and T=512 as fractions of HBM bandwidth, and the CPU
-oracle timed on a bounded token sample of the same workload.
+small-batch sweep, T=64 and T=512 as fractions of HBM bandwidth, the skewed
+routing stress layer at T=16384 with its expert load, and the CPU oracle timed
+on a bounded token sample of the same workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -236,6 +237,52 @@ def bench_routing_ablation(cfg, steps, warmup):
             "outputs_bitwise_equal": same, "timing": f"eager launches, wall clock, mean of {steps} layers"}
 
 
+def bench_skewed(cfg, reps=10):
+    """The skewed-routing stress layer (per-expert Zipf logit bias, T=16384):
+    throughput and MFMA fraction of the whole layer (HIP graph replays), the
+    two grouped GEMMs' stage times, and the expert load it produced (max/mean
+    rows, empty experts, routed tiles of the block map)."""
+    import torch
+    import sparse_moe_softmax_amd as moe
+    import synth
+    d = cfg.dims
+    md = moe.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+    log(f"skewed {cfg.name}: generating weights (seed {cfg.seed})")
+    lay = synth.make_layer(d, cfg.seed, zipf_bias=cfg.zipf_bias, device="cuda")
+    dl = device_layer(lay, d, moe)
+    x = synth.activations(cfg.T, d.hidden, cfg.seed).cuda()
+    ws = moe.moe_workspace(md, cfg.T)
+    y = torch.empty((cfg.T, d.hidden), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((cfg.T, d.top_k), dtype=torch.int32, device="cuda")
+    moe.moe_forward(md, dl, x, y=y, ids_out=ids, workspace=ws)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(md, dl, x, y=y, workspace=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    stages = time_stages(moe, md, dl, x, y, ws, reps=reps)
+    counts = torch.bincount(ids.flatten().cpu().long(), minlength=d.n_experts)
+    bm = moe.moe_block_m()
+    tiles = int(((counts + bm - 1) // bm).sum())
+    tflops = layer_flops_per_token(d) * cfg.T / (us * 1e-6) / 1e12
+    log(f"skewed {cfg.name}: {us:.1f} us per layer, max/mean load {counts.max().item() / counts.float().mean().item():.1f}")
+    return {"workload": f"moe_layer_prefill_{cfg.name}", "tokens": cfg.T, "us_per_layer": round(us, 2),
+            "tokens_per_s": round(cfg.T / (us * 1e-6), 1), "layer_tflops": round(tflops, 2),
+            "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "gate_up_us": round(stages["gate_up"], 2), "down_us": round(stages["down"], 2),
+            "max_over_mean_load": round(counts.max().item() / counts.float().mean().item(), 2),
+            "empty_experts": int((counts == 0).sum()), "experts_above_10x_mean":
+                int((counts > 10 * counts.float().mean()).sum()), "routed_tiles": tiles, "block_m": bm,
+            "launch": f"whole layer as one HIP graph, mean of {reps} replays"}
+
+
 def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20, seeds=None):
     """Memory-bound batch sizes: one pass of T tokens over n_layers distinct
     layers per replay (a HIP graph), algorithmic bytes = the experts the tokens
@@ -383,7 +430,14 @@ def cpu_baseline(res, sample, threads, min_secs=10.0, max_passes=8):
     max_rel = float(np.abs(g - o).max() / np.abs(o).max())
     l1_rel = float(np.abs(g - o).sum() / np.abs(o).sum())
     log(f"cpu baseline: {secs:.2f} s; parity max_rel {max_rel:.2e} l1_rel {l1_rel:.2e} ids_equal {ids_equal}")
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return ({"value": round(passes * sample / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+             "cpu_model": cpu_model,
              "sample": f"{sample} of the {cfg.T} tokens of the same layer (router, top-k, experts incl. "
                        f"dequantisation of the experts they touch, combine), {passes} pass(es), {secs:.1f} s"},
             {"tokens": sample, "logit_max_abs_err": logit_err, "ids_equal_given_gpu_logits": ids_equal,
@@ -465,6 +519,8 @@ def main():
         # its own configuration) on the same footing: algorithmic bytes / time
         mid = {c.T: c.seed for c in (synth.CONFIGS["t64"], synth.CONFIGS["t512"])}
         out["hbm_bound_prefill"] = bench_small_t(synth.CONFIGS["t512"], Ts=tuple(sorted(mid)), seeds=mid)
+        if cfg.name != "skew16k":
+            out["skewed_routing"] = bench_skewed(synth.CONFIGS["skew16k"])
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"], out["parity_sample"] = cpu_baseline(res, args.cpu_sample, threads)
