@@ -462,7 +462,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py times the MoE layer on one GPU; --gpus {args.gpus} (world size {world}) is not "
-              f"supported: this build runs on a single MI355X", file=sys.stderr)
+              f"supported: the layer is timed on a single MI355X", file=sys.stderr)
         sys.exit(2)
 
     import torch
