@@ -338,7 +338,10 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
                       "router gemm")))
     return st;
   if (run(MOE_STAGE_TOPK) &&
-      (st = hip_check(launch_topk(rout, sout, S, L->router_bias, T, E, k, logits, s_logit, ids, wts, gate, tilehist, s),
+      // with K splits top-k forms the final logits; they are stored only when
+      // the caller asked for them (nothing downstream reads them)
+      (st = hip_check(launch_topk(rout, sout, S, L->router_bias, T, E, k, S > 1 ? logits_out : logits, s_logit, ids,
+                                  wts, gate, tilehist, s),
                       "top-k")))
     return st;
   if (run(MOE_STAGE_GROUP) &&
