@@ -349,6 +349,21 @@ def test_forward_parity_large_sampled(cfg):
     say("errors", r["errs"])
 
 
+def test_forward_parity_max_tokens():
+    """The largest batch the API accepts (65536 tokens, the model's dims):
+    logits and routing of every token against the oracle (ids bit for bit),
+    the layer output on 48 sampled tokens including the first and the last."""
+    d, T, seed = MODEL, 65536, 107
+    say("forward max tokens", T)
+    lay = synth.make_layer(d, seed)
+    x = synth.activations(T, d.hidden, seed)
+    rng = np.random.default_rng(seed)
+    tokens = np.sort(rng.choice(T, 48, replace=False)).astype(np.int32)
+    tokens[0], tokens[-1] = 0, T - 1
+    r = gu.forward_and_check(d, lay, x, tokens=tokens)
+    say("errors", r["errs"])
+
+
 @pytest.mark.parametrize("cfg", ["t64", "t512"])
 def test_forward_parity_configs(cfg):
     c = synth.CONFIGS[cfg]
