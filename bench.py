@@ -73,6 +73,22 @@ def device_layer(lay, d, moe, pack=True):
                             t(lay.shared_gate_w), t(lay.router_bias), pack=pack)
 
 
+def warm_graph(g, min_replays, min_seconds=0.025):
+    """Untimed replays of graph g until the work runs at its steady rate: at
+    least min_replays, and at least min_seconds of replays (the first ~20 ms
+    of back-to-back work after a capture run several per cent slower)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            g.replay()
+        n += 8
+        torch.cuda.synchronize()
+        if n >= min_replays and time.perf_counter() - t0 >= min_seconds:
+            return n
+
+
 def time_stages(moe, md, dl, x, y, ws, reps):
     """Average GPU time (us) of each stage of the layer, measured inside whole
     layers: HIP events recorded between the stages on the launch stream."""
@@ -123,9 +139,7 @@ def bench_prefill(cfg, steps, warmup):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         moe.moe_forward(md, dl, x, y=y, workspace=ws)
-    for _ in range(max(1, warmup)):
-        g.replay()
-    torch.cuda.synchronize()
+    warm_graph(g, max(48, warmup))   # untimed, until the layer runs at its steady rate
     t0 = time.perf_counter()
     e0.record(s)
     for _ in range(steps):
@@ -135,6 +149,15 @@ def bench_prefill(cfg, steps, warmup):
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1000.0 / steps
     gpu_ms = e0.elapsed_time(e1) / steps
+    # the spread: the same replays again, an event between every two
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(s)
+    for i in range(steps):
+        g.replay()
+        ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps))
+    pct = {f"p{q}": round(per[min(steps - 1, int(q / 100 * steps))], 2) for q in (10, 50, 90)}
     log(f"prefill {cfg.name}: {wall_ms:.4f} ms/step wall, {gpu_ms:.4f} ms/step gpu events (HIP graph); "
         f"eager launches {eager_ms:.4f} ms/step")
     stages = time_stages(moe, md, dl, x, y, ws, reps=max(10, steps))
@@ -143,7 +166,7 @@ def bench_prefill(cfg, steps, warmup):
     moe.moe_forward(md, dl, x, y=y, logits_out=logits, ids_out=ids, workspace=ws)
     torch.cuda.synchronize()
     return {"cfg": cfg, "lay": lay, "x_cpu": x_cpu, "wall_ms": wall_ms, "gpu_ms": gpu_ms, "eager_ms": eager_ms,
-            "stages": stages, "y": y, "logits": logits, "ids": ids}
+            "pct_us": pct, "stages": stages, "y": y, "logits": logits, "ids": ids}
 
 
 def bench_decode(cfg, n_steps, graph_chunk=32):
@@ -258,8 +281,7 @@ def bench_skewed(cfg, reps=10):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         moe.moe_forward(md, dl, x, y=y, workspace=ws)
-    g.replay()
-    torch.cuda.synchronize()
+    warm_graph(g, 8)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -312,8 +334,7 @@ def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20, seeds=None):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             one_pass()
-        g.replay()
-        torch.cuda.synchronize()
+        warm_graph(g, 8)
         s_ = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s_)
@@ -502,7 +523,8 @@ def main():
                        "frac_of_bf16_peak": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
                        "gpu_ms_per_step": round(res["gpu_ms"], 5),
                        "launch": "whole layer as one HIP graph, replayed",
-                       "eager_ms_per_step": round(res["eager_ms"], 5)},
+                       "eager_ms_per_step": round(res["eager_ms"], 5),
+                       "us_per_replay_percentiles": res["pct_us"]},
         "stages_us": {k: round(v, 2) for k, v in res["stages"].items()},
         "roofline": {"bound": "mfma", "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
