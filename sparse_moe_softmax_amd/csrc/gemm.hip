@@ -260,6 +260,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
     for (int c = 0; c < 2; ++c) bq[0][c] = dq(raw[0], c, 0);
     // k-step q of the stage: K block q / 4, k-step q % 4 within it
+    // Each SIMD holds one wave of each of the CU's two workgroups, and a wave
+    // does not issue its own VALU work while its own MFMA runs: the matrix
+    // core is kept busy by the other wave's MFMAs.  In the gate/up GEMM the
+    // wave in its MFMA section issues ahead of the other wave's set-up work
+    // (barrier, load issue, fragment reads); the down GEMM's short K loops
+    // lose by it, so there the priority stays even.
+    if constexpr (MODE == kSwiglu) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = 0; q < 4 * KS; ++q) {
       const int nu = (q + 1) >> 2, nks = (q + 1) & 3;
@@ -272,6 +279,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if constexpr (MODE == kSwiglu) __builtin_amdgcn_s_setprio(0);
   };
 
   // Short tiles (1-2 sub-tiles) have registers to spare, and their iteration
