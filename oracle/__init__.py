@@ -71,6 +71,7 @@ def _declare(lib):
         "oracle_grouped_swiglu": [_I64, _I64, _I64, _I64, _I64, _P, _INT, _P, _P, _P, _P, _P, _P, _INT],
         "oracle_grouped_down": [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _INT],
         "oracle_moe_tokens": [_I64] * 6 + [_P] * 16 + [_P, _I64, _P, _P, _P, _P, _INT],
+        "oracle_gqa_decode": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_double, _P, _INT],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -291,3 +292,26 @@ def layer(d: Dims, x_bits, lw: LayerWeights, tokens=None, logits=None, s=None, t
     g = sigmoid(s)
     out, _, _, _ = moe_tokens(d, x_bits, ids, w, g, lw, tokens=tokens, threads=threads)
     return {"logits": logits, "s": s, "ids": ids, "w": w, "g": g, "out": out}
+
+
+# --------------------------------------------------------------------- attention
+
+def gqa_decode(q_bits, k_bits, v_bits, lens, scale: float, threads: int = 0) -> np.ndarray:
+    """One decode step of grouped-query attention, [B][Hq][D] float64 (unrounded).
+
+    q_bits [B][Hq][D], k_bits / v_bits [B][Hkv][S][D] (bf16 bit patterns),
+    lens [B] positions in use.  Query head h reads key/value head h // (Hq // Hkv)
+    (Lily page, section "The architecture that forces the issue": 16 query heads
+    share 2 key/value heads)."""
+    q_bits = _c(q_bits, np.uint16)
+    k_bits = _c(k_bits, np.uint16)
+    v_bits = _c(v_bits, np.uint16)
+    lens = _c(lens, np.int32)
+    B, Hq, D = q_bits.shape
+    _, Hkv, S, _ = k_bits.shape
+    assert k_bits.shape == (B, Hkv, S, D) and v_bits.shape == k_bits.shape and lens.shape == (B,)
+    assert Hq % Hkv == 0 and np.all((lens >= 0) & (lens <= S))
+    out = np.empty((B, Hq, D), np.float64)
+    _lib().oracle_gqa_decode(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(lens), B, Hq, Hkv, S, D,
+                             float(scale), _ptr(out), threads)
+    return out

@@ -28,6 +28,17 @@
 //
 // Built with g++ -O2 -ffp-contract=off (no fast-math).  Threads only split
 // independent tokens or experts; they never change an arithmetic order.
+//
+// Also here: one decode step of grouped-query attention (oracle_gqa_decode),
+// the attention the same model runs in its full-attention layers (Lily page,
+// section "The architecture that forces the issue": 16 query heads share 2
+// key/value heads) and whose packed form the "Inside Lily ..." page lists
+// among its optimisations (section "Key Optimizations at a Glance", GQA
+// packing).  The pages give no formula; the reading is the standard one
+// written out below: query head h reads key/value head h / (Hq / Hkv), scores
+// are scale * (q . k_p) over the L cached positions of its sequence, softmax
+// over those positions, output the softmax-weighted sum of the value rows, in
+// double, rounded once to bfloat16 by the caller's comparison.
 
 #include <algorithm>
 #include <atomic>
@@ -443,6 +454,45 @@ void oracle_moe_tokens(int64_t H, int64_t I, int64_t E, int64_t k, int64_t G, in
       out[i * H + m] = bf16_bits(round_bf16(y[m]));
       if (y_out) y_out[i * H + m] = y[m];
     }
+  });
+}
+
+
+// One decode step of grouped-query attention for B sequences.
+//   q   [B][Hq][D] bf16 bits, k/v [B][Hkv][S][D] bf16 bits (S cached positions
+//   per sequence and head), lens[B] positions in use (0 <= lens[b] <= S).
+//   out [B][Hq][D] double: for query head h of sequence b, with kv = h / (Hq/Hkv),
+//   s_p = scale * sum_d q[d] k[p][d]  (p < lens[b]),
+//   out = sum_p exp(s_p - max s) v[p] / sum_p exp(s_p - max s);
+//   a sequence with no positions gives zeros.
+void oracle_gqa_decode(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* lens, int64_t B,
+                       int64_t Hq, int64_t Hkv, int64_t S, int64_t D, double scale, double* out, int n_threads) {
+  const int64_t group = Hq / Hkv;
+  parallel_for(B * Hq, n_threads, [&](int64_t bh) {
+    const int64_t b = bh / Hq, h = bh % Hq, kv = h / group;
+    const int64_t L = lens[b];
+    double* o = out + bh * D;
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    if (L <= 0) return;
+    const uint16_t* qh = q + bh * D;
+    const uint16_t* kh = kc + (b * Hkv + kv) * S * D;
+    const uint16_t* vh = vc + (b * Hkv + kv) * S * D;
+    std::vector<double> sc(L);
+    double m = -INFINITY;
+    for (int64_t p = 0; p < L; ++p) {
+      double dot = 0.0;
+      for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(qh[d]) * bf16_to_double(kh[p * D + d]);
+      sc[p] = scale * dot;
+      m = std::max(m, sc[p]);
+    }
+    double den = 0.0;
+    for (int64_t p = 0; p < L; ++p) {
+      sc[p] = std::exp(sc[p] - m);
+      den += sc[p];
+    }
+    for (int64_t p = 0; p < L; ++p)
+      for (int64_t d = 0; d < D; ++d) o[d] += sc[p] * bf16_to_double(vh[p * D + d]);
+    for (int64_t d = 0; d < D; ++d) o[d] /= den;
   });
 }
 

@@ -361,3 +361,108 @@ def test_layer_full_dims_few_tokens(oracle_lib):
     out_ref, _ = refs.layer_ref(x, res["ids"], res["w"], res["g"], W, d)
     assert np.array_equal(oracle.bf16_to_double(res["out"]), out_ref)
     assert np.allclose(res["w"].sum(1), 1.0, atol=1e-6)
+
+
+# ------------------------------------------------------------------ grouped-query decode attention
+
+def _bf16_bits_of(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+
+
+def _attn_case(B, Hq, Hkv, S, D, seed):
+    g = np.random.default_rng(seed)
+    q = _bf16_bits_of(g.standard_normal((B, Hq, D)))
+    k = _bf16_bits_of(g.standard_normal((B, Hkv, S, D)))
+    v = _bf16_bits_of(g.standard_normal((B, Hkv, S, D)))
+    return q, k, v
+
+
+def test_gqa_single_position_returns_its_value_row(oracle_lib):
+    """One cached position: its softmax weight is 1, so every query head of the
+    group returns that value row exactly."""
+    q, k, v = _attn_case(2, 16, 2, 5, 64, 1)
+    out = oracle.gqa_decode(q, k, v, np.array([1, 1], np.int32), 0.125)
+    vd = oracle.bf16_to_double(v)
+    for h in range(16):
+        assert np.array_equal(out[:, h], vd[:, h // 8, 0])
+
+
+def test_gqa_equal_keys_average_the_values(oracle_lib):
+    """All keys equal: every score is equal, so the output is the plain mean of
+    the value rows in use."""
+    q, k, v = _attn_case(1, 8, 2, 37, 128, 2)
+    k[:] = k[:, :, :1, :]
+    L = 29
+    out = oracle.gqa_decode(q, k, v, np.array([L], np.int32), 0.0883883)
+    mean = oracle.bf16_to_double(v)[0, :, :L].mean(axis=1)          # [Hkv][D]
+    for h in range(8):
+        assert np.allclose(out[0, h], mean[h // 4], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (8, 4), (4, 4)])
+def test_gqa_head_mapping_contiguous_groups(oracle_lib, Hq, Hkv):
+    """Value rows of key/value head j are the constant (j + 1) / 4: query head h
+    must return h // (Hq / Hkv) + 1 over 4 (a mapping h % Hkv fails for Hkv > 1
+    and Hq > Hkv)."""
+    q, k, v = _attn_case(1, Hq, Hkv, 19, 64, 3)
+    for j in range(Hkv):
+        v[0, j] = _bf16_bits_of(np.full((19, 64), (j + 1) / 4.0))
+    out = oracle.gqa_decode(q, k, v, np.array([19], np.int32), 0.125)
+    for h in range(Hq):
+        assert np.allclose(out[0, h], (h // (Hq // Hkv) + 1) / 4.0, rtol=0, atol=1e-14)
+
+
+def test_gqa_two_positions_logistic_closed_form(oracle_lib):
+    """Two positions: out = v0 + sigmoid(scale * q.(k1 - k0)) * (v1 - v0), the dot
+    products summed exactly with math.fsum."""
+    q, k, v = _attn_case(1, 2, 1, 2, 64, 4)
+    scale = 0.3
+    out = oracle.gqa_decode(q, k, v, np.array([2], np.int32), scale)
+    qd, kd, vd = oracle.bf16_to_double(q)[0], oracle.bf16_to_double(k)[0, 0], oracle.bf16_to_double(v)[0, 0]
+    for h in range(2):
+        delta = scale * (math.fsum(qd[h] * kd[1]) - math.fsum(qd[h] * kd[0]))
+        sig = 1.0 / (1.0 + math.exp(-delta))
+        assert np.allclose(out[0, h], vd[0] + sig * (vd[1] - vd[0]), rtol=0, atol=1e-13)
+
+
+def test_gqa_dominant_key_selects_its_row(oracle_lib):
+    """A key equal to 64 times the query outscores every other position by
+    hundreds: the output is that position's value row to double precision."""
+    q, k, v = _attn_case(1, 1, 1, 50, 64, 5)
+    k = _bf16_bits_of(oracle.bf16_to_double(k) * 0.01)
+    k[0, 0, 31] = _bf16_bits_of(64.0 * oracle.bf16_to_double(q)[0, 0])
+    out = oracle.gqa_decode(q, k, v, np.array([50], np.int32), 1.0)
+    assert np.allclose(out[0, 0], oracle.bf16_to_double(v)[0, 0, 31], rtol=1e-12, atol=0)
+
+
+def test_gqa_reads_only_positions_in_use(oracle_lib):
+    """Positions at or past a sequence's length hold NaN: the output stays finite
+    and equals the result on the cache cut to that length; length 0 gives zeros."""
+    q, k, v = _attn_case(3, 4, 2, 40, 64, 6)
+    lens = np.array([40, 13, 0], np.int32)
+    for b in range(3):
+        k[b, :, lens[b]:] = 0x7FC0
+        v[b, :, lens[b]:] = 0x7FC0
+    out = oracle.gqa_decode(q, k, v, lens, 0.125)
+    assert np.all(np.isfinite(out))
+    assert np.array_equal(out[2], np.zeros((4, 64)))
+    cut = oracle.gqa_decode(q[1:2], k[1:2, :, :13].copy(), v[1:2, :, :13].copy(), np.array([13], np.int32), 0.125)
+    assert np.array_equal(out[1], cut[0])
+
+
+def test_gqa_matches_torch_sdpa_float64(oracle_lib):
+    """torch's scaled_dot_product_attention in float64 with enable_gqa (query
+    heads grouped onto key/value heads by h // (Hq / Hkv)), ragged lengths."""
+    import torch.nn.functional as F
+    B, Hq, Hkv, S, D = 3, 16, 2, 70, 128
+    q, k, v = _attn_case(B, Hq, Hkv, S, D, 7)
+    lens = np.array([70, 1, 33], np.int32)
+    scale = 1.0 / math.sqrt(D)
+    out = oracle.gqa_decode(q, k, v, lens, scale)
+    qd, kd, vd = (torch.from_numpy(oracle.bf16_to_double(a)) for a in (q, k, v))
+    for b in range(B):
+        L = int(lens[b])
+        ref = F.scaled_dot_product_attention(qd[b:b + 1, :, None, :], kd[b:b + 1, :, :L], vd[b:b + 1, :, :L],
+                                             scale=scale, enable_gqa=True)[0, :, 0]
+        assert np.allclose(out[b], ref.numpy(), rtol=1e-12, atol=1e-14)
