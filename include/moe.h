@@ -278,6 +278,34 @@ moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* layer, c
                                     uint16_t* y, int32_t* ids_out, float* w_out, void* workspace,
                                     size_t workspace_bytes, void* host_buf, size_t host_bytes, void* stream);
 
+/* Grouped-query attention, one decode step (one query row per head) for B
+ * sequences.  The model's full-attention layers have 16 query heads sharing 2
+ * key/value heads (Lily page, section "The architecture that forces the
+ * issue"); the "Inside Lily ..." page (section "Key Optimizations at a Glance")
+ * names GQA packing, one load of each key/value row for all the query heads of
+ * its group, among its optimisations.
+ *   q [B][Hq][D] bf16; k_cache, v_cache [B][Hkv][S][D] bf16 (16-byte aligned),
+ *   S positions of capacity per sequence and head; seq_lens [B] int32 positions
+ *   in use (values are clamped to [0, S]); out [B][Hq][D] bf16.
+ *   Query head h reads key/value head h / (Hq / Hkv):
+ *   out = sum_p softmax_p(scale * q . k_p) v_p over p < seq_lens[b], scores,
+ *   softmax and sums in fp32, one bf16 rounding; a sequence of length 0 gives
+ *   zeros.  The positions are cut into ranges that run in parallel; their
+ *   partial results are merged in range order, so out is reproducible.
+ *   pack_heads = 1: a workgroup takes all Hq / Hkv query heads of a group and
+ *   loads each key/value row once; pack_heads = 0: one query head per
+ *   workgroup, each row loaded once per query head (the unpacked form, kept to
+ *   measure what packing saves).
+ * Supported: Hq % Hkv == 0, Hq / Hkv <= 8, D in {64, 128, 256}, 1 <= B <= 4096,
+ * 1 <= S <= 2^22.  workspace (16-byte aligned) of at least
+ * moe_gqa_decode_workspace_bytes(B, Hq, Hkv, D, S) bytes; 0 for an unsupported
+ * shape. */
+size_t moe_gqa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S);
+moe_status moe_gqa_decode_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                    const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S,
+                                    float scale, int32_t pack_heads, uint16_t* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status; message of the last failed check on this thread. */
 const char* moe_status_str(moe_status s);
 const char* moe_last_error_message(void);

@@ -10,6 +10,7 @@ call raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 
@@ -20,6 +21,7 @@ __all__ = [
     "moe_router_logits", "moe_route", "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4",
     "moe_workspace_bytes", "moe_workspace", "moe_forward", "moe_forward_stages", "moe_packed_q4_bytes",
     "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes", "moe_forward_host_routing",
+    "moe_gqa_decode_workspace_bytes", "moe_gqa_decode_attention",
     "MOE_EPI_SWIGLU_BF16",
     "MOE_EPI_WEIGHTED_SCATTER_F32", "STAGES",
     "EXPORTED_SYMBOLS",
@@ -37,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4", "moe_workspace_bytes", "moe_forward",
     "moe_forward_stages", "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
     "moe_packed_q4_bytes", "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes",
-    "moe_forward_host_routing",
+    "moe_forward_host_routing", "moe_gqa_decode_workspace_bytes", "moe_gqa_decode_attention",
 )
 
 
@@ -105,6 +107,9 @@ def lib():
             "moe_host_block_map": ([_P, _I32, _I32, _I32, _P, _P, _P], _I32),
             "moe_host_routing_bytes": ([PD, _I32], _SZ),
             "moe_forward_host_routing": ([PD, PL, _P, _I32, _P, _P, _P, _P, _SZ, _P, _SZ, _P], _I32),
+            "moe_gqa_decode_workspace_bytes": ([_I32] * 5, _SZ),
+            "moe_gqa_decode_attention": ([_P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, _I32, _P, _P, _SZ, _P],
+                                         _I32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(h, name)
@@ -332,3 +337,34 @@ def moe_forward_stages(d, layer: LayerWeights, x: torch.Tensor, y: torch.Tensor,
                                     _ptr(logits_out), _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(),
                                     first, last, _stream()))
     return y
+
+
+# ------------------------------------------------------------------ grouped-query decode attention
+
+def moe_gqa_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, S: int) -> int:
+    return lib().moe_gqa_decode_workspace_bytes(B, Hq, Hkv, D, S)
+
+
+def moe_gqa_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                             scale: float | None = None, pack_heads: bool = True, out=None, workspace=None):
+    """One decode step of grouped-query attention.  q [B][Hq][D] bf16, k_cache /
+    v_cache [B][Hkv][S][D] bf16, seq_lens [B] int32 (device).  Returns out
+    [B][Hq][D] bf16.  scale defaults to 1/sqrt(D)."""
+    B, Hq, D = q.shape
+    Bk, Hkv, S, Dk = k_cache.shape
+    if (Bk, Dk) != (B, D) or v_cache.shape != k_cache.shape or tuple(seq_lens.shape) != (B,):
+        raise ValueError("shapes: q [B][Hq][D], caches [B][Hkv][S][D], seq_lens [B]")
+    for t, dt in ((q, torch.bfloat16), (k_cache, torch.bfloat16), (v_cache, torch.bfloat16), (seq_lens, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError("q and caches must be contiguous bf16, seq_lens contiguous int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = _empty((B, Hq, D), torch.bfloat16, q)
+    if workspace is None:
+        need = moe_gqa_decode_workspace_bytes(B, Hq, Hkv, D, S)
+        workspace = _empty((max(need, 1),), torch.uint8, q)
+    _check(lib().moe_gqa_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, Hq, Hkv, D, S,
+                                          float(scale), 1 if pack_heads else 0, _ptr(out), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream()))
+    return out

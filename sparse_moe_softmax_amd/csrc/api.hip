@@ -452,4 +452,39 @@ moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* L, const
                             MOE_STAGE_COMBINE, stream);
 }
 
+// ------------------------------------------------------------------ grouped-query decode attention
+
+namespace {
+moe_status check_gqa(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S) {
+  if (B < 1 || B > 4096 || Hq < 1 || Hkv < 1 || S < 1 || S > (1 << 22))
+    return fail(MOE_ERR_INVALID_ARG, "gqa: need 1 <= B <= 4096, Hq, Hkv >= 1, 1 <= S <= 2^22");
+  if (Hq % Hkv) return fail(MOE_ERR_INVALID_ARG, "gqa: Hq %% Hkv != 0");
+  if (Hq / Hkv > 8 || Hq > 1024) return fail(MOE_ERR_UNSUPPORTED, "gqa: at most 8 query heads per key/value head");
+  if (D != 64 && D != 128 && D != 256) return fail(MOE_ERR_UNSUPPORTED, "gqa: head_dim must be 64, 128 or 256");
+  return MOE_OK;
+}
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+}  // namespace
+
+size_t moe_gqa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S) {
+  if (check_gqa(B, Hq, Hkv, D, S)) return 0;
+  return gqa_workspace_bytes(B, Hq, Hkv, S, D);
+}
+
+moe_status moe_gqa_decode_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                    const int32_t* seq_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t S,
+                                    float scale, int32_t pack_heads, uint16_t* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  moe_status st = check_gqa(B, Hq, Hkv, D, S);
+  if (st) return st;
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return fail(MOE_ERR_INVALID_ARG, "gqa: NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(MOE_ERR_INVALID_ARG, "gqa: caches not 16-byte aligned");
+  if (pack_heads != 0 && pack_heads != 1) return fail(MOE_ERR_INVALID_ARG, "gqa: pack_heads must be 0 or 1");
+  if (!workspace || !aligned16(workspace) || workspace_bytes < gqa_workspace_bytes(B, Hq, Hkv, S, D))
+    return fail(MOE_ERR_WORKSPACE, "gqa: workspace missing, unaligned or smaller than moe_gqa_decode_workspace_bytes");
+  return hip_check(launch_gqa_decode(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, D, S, scale, pack_heads == 1, out,
+                                     workspace, static_cast<hipStream_t>(stream)),
+                   "gqa decode");
+}
+
 }  // extern "C"

@@ -125,6 +125,16 @@ def activations(T: int, H: int, seed: int, step: int = 0) -> torch.Tensor:
     return x.to(torch.bfloat16)
 
 
+def gqa_decode_inputs(B: int, Hq: int, Hkv: int, S: int, D: int, seed: int, layer: int = 0, q_std: float = 1.0):
+    """One decode step of grouped-query attention on the CPU: q [B][Hq][D] ~ N(0, q_std^2)
+    and k, v caches [B][Hkv][S][D] ~ N(0, 1), each rounded to bfloat16."""
+    g = _cpu_gen(seed, 9, layer)
+    q = (torch.randn(B, Hq, D, generator=g, dtype=torch.float32) * q_std).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, S, D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, S, D, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v
+
+
 def router_weights(E: int, H: int, seed: int, layer: int = 0) -> torch.Tensor:
     """W_r ~ N(0, 1/H) fp32 [E][H], on the CPU."""
     return torch.randn(E, H, generator=_cpu_gen(seed, 2, layer), dtype=torch.float32) * (1.0 / math.sqrt(H))

@@ -201,3 +201,26 @@ def test_host_routing_checks(m):
                                           need, None) == -2
     assert L.moe_forward_host_routing(d, ctypes.byref(layer), FAKE, 512, FAKE, None, None, FAKE, 1 << 30, vp(hb),
                                       need - 4, None) == -1
+
+
+# ------------------------------------------------------------------ grouped-query decode attention (host checks)
+
+def test_gqa_workspace_and_checks(m):
+    L = m.lib()
+    # 32768 positions, 2 key/value heads: 1024 steps of 64 -> 2 per range, 256 ranges
+    assert L.moe_gqa_decode_workspace_bytes(1, 16, 2, 256, 32768) == 16 * 256 * (256 + 2) * 4
+    assert L.moe_gqa_decode_workspace_bytes(1, 16, 2, 96, 100) == 0          # head_dim
+    assert L.moe_gqa_decode_workspace_bytes(1, 18, 2, 128, 100) == 0         # 9 query heads per group
+    need = L.moe_gqa_decode_workspace_bytes(2, 16, 2, 128, 1000)
+    assert need > 0
+    call = lambda Hq, Hkv, D, ws, nbytes, pack=1, k=FAKE: L.moe_gqa_decode_attention(
+        FAKE, k, FAKE, FAKE, 2, Hq, Hkv, D, 1000, 0.1, pack, FAKE, ws, nbytes, None)
+    assert call(16, 2, 96, FAKE, need) == -2
+    assert call(16, 3, 128, FAKE, need) == -1
+    assert call(18, 2, 128, FAKE, need) == -2
+    assert call(16, 2, 128, FAKE, need - 1) == -3
+    assert call(16, 2, 128, None, need) == -3
+    assert call(16, 2, 128, FAKE, need, pack=2) == -1
+    assert call(16, 2, 128, FAKE, need, k=ctypes.c_void_p(4100)) == -1       # cache not 16-byte aligned
+    assert L.moe_gqa_decode_attention(FAKE, FAKE, FAKE, None, 2, 16, 2, 128, 1000, 0.1, 1, FAKE, FAKE, need,
+                                      None) == -1
