@@ -357,6 +357,55 @@ def bench_small_t(cfg, Ts=(1, 2, 4, 8, 16), n_layers=8, reps=20, seeds=None):
             "points": out}
 
 
+def bench_gqa_decode(n_layers=10, B=1, Hq=16, Hkv=2, D=256, S=32768, reps=20, seed=109):
+    """Grouped-query decode attention at 32K context, one query row per head:
+    a HIP graph of one call per attention layer (n_layers distinct key/value
+    caches, together larger than the 256 MB Infinity Cache), replayed; packed
+    (each key/value row loaded once per group) and unpacked (once per query
+    head).  Algorithmic bytes per call: the K and V rows in use, q and out."""
+    import torch
+    import sparse_moe_softmax_amd as moe
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    draw = lambda *shape: torch.randn(*shape, generator=gen, device="cuda").to(torch.bfloat16)
+    qs = [draw(B, Hq, D) for _ in range(n_layers)]
+    ks = [draw(B, Hkv, S, D) for _ in range(n_layers)]
+    vs = [draw(B, Hkv, S, D) for _ in range(n_layers)]
+    lens = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.moe_gqa_decode_workspace_bytes(B, Hq, Hkv, D, S), dtype=torch.uint8, device="cuda")
+    outs = torch.empty((n_layers, B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    us = {}
+    for pack in (True, False):
+        def one_pass():
+            for l in range(n_layers):
+                moe.moe_gqa_decode_attention(qs[l], ks[l], vs[l], lens, pack_heads=pack, out=outs[l], workspace=ws)
+
+        one_pass()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_pass()
+        warm_graph(g, 8)
+        s_ = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s_)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s_)
+        torch.cuda.synchronize()
+        us[pack] = e0.elapsed_time(e1) * 1000.0 / reps / n_layers
+    nbytes = 2 * B * Hkv * S * D * 2 + 2 * B * Hq * D * 2
+    gbs = nbytes / (us[True] * 1e-6) / 1e9
+    log(f"gqa decode S={S}: packed {us[True]:.2f} us ({gbs:.0f} GB/s), unpacked {us[False]:.2f} us")
+    return {"workload": f"GQA decode attention, batch {B}, {Hq} query heads on {Hkv} key/value heads, "
+                        f"head_dim {D}, context {S}",
+            "layers": n_layers, "launch": f"HIP graph of one call per layer, {reps} replays",
+            "us_per_call": round(us[True], 3), "bytes_per_call": nbytes, "GBs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "unpacked_us_per_call": round(us[False], 3),
+            "packing_speedup": round(us[False] / us[True], 3)}
+
+
 GEMM_SOURCES = ("sparse_moe_softmax_amd/csrc/gemm.hip", "sparse_moe_softmax_amd/csrc/internal.hpp")
 TRAFFIC_PROFILE = "profiles/gemm_gate_up_t4096_hbm_traffic.md"
 
@@ -478,7 +527,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the routing ablation and the small-T sweep")
     ap.add_argument("--cpu-sample", type=int, default=4096)
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--profile-stage", default=None, help="profiling run: one stage repeated, no JSON line")
+    ap.add_argument("--profile-stage", default=None,
+                    help="profiling run: one stage repeated, no JSON line (gqa_decode: the attention leg alone)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -492,6 +542,9 @@ def main():
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[args.workload]
     d = cfg.dims
+    if args.profile_stage == "gqa_decode":
+        print(json.dumps({"gqa_decode_attention": bench_gqa_decode(reps=args.steps)}), flush=True)
+        return
     if args.profile_stage:
         profile_stage(cfg, args.profile_stage, args.steps)
         return
@@ -543,6 +596,7 @@ def main():
         out["hbm_bound_prefill"] = bench_small_t(synth.CONFIGS["t512"], Ts=tuple(sorted(mid)), seeds=mid)
         if cfg.name != "skew16k":
             out["skewed_routing"] = bench_skewed(synth.CONFIGS["skew16k"])
+        out["gqa_decode_attention"] = bench_gqa_decode()
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"], out["parity_sample"] = cpu_baseline(res, args.cpu_sample, threads)

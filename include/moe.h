@@ -284,7 +284,7 @@ moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* layer, c
  * issue"); the "Inside Lily ..." page (section "Key Optimizations at a Glance")
  * names GQA packing, one load of each key/value row for all the query heads of
  * its group, among its optimisations.
- *   q [B][Hq][D] bf16; k_cache, v_cache [B][Hkv][S][D] bf16 (16-byte aligned),
+ *   q [B][Hq][D] bf16 (4-byte aligned); k_cache, v_cache [B][Hkv][S][D] bf16 (16-byte aligned),
  *   S positions of capacity per sequence and head; seq_lens [B] int32 positions
  *   in use (values are clamped to [0, S]); out [B][Hq][D] bf16.
  *   Query head h reads key/value head h / (Hq / Hkv):

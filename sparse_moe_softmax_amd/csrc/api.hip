@@ -479,6 +479,7 @@ moe_status moe_gqa_decode_attention(const uint16_t* q, const uint16_t* k_cache, 
   if (st) return st;
   if (!q || !k_cache || !v_cache || !seq_lens || !out) return fail(MOE_ERR_INVALID_ARG, "gqa: NULL pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(MOE_ERR_INVALID_ARG, "gqa: caches not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(q) & 3u) return fail(MOE_ERR_INVALID_ARG, "gqa: q not 4-byte aligned");
   if (pack_heads != 0 && pack_heads != 1) return fail(MOE_ERR_INVALID_ARG, "gqa: pack_heads must be 0 or 1");
   if (!workspace || !aligned16(workspace) || workspace_bytes < gqa_workspace_bytes(B, Hq, Hkv, S, D))
     return fail(MOE_ERR_WORKSPACE, "gqa: workspace missing, unaligned or smaller than moe_gqa_decode_workspace_bytes");

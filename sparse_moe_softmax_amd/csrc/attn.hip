@@ -28,15 +28,19 @@ namespace {
 
 constexpr int kAtSub = 64;        // positions staged per step
 constexpr int kAtThreads = 256;
+constexpr int kMgThreads = 256;   // merge
 constexpr int kAtGroup = 8;       // query heads per workgroup at most
-constexpr int kAtTarget = 512;    // workgroups wanted per launch (two per CU)
+#ifndef MOE_GQA_TARGET
+#define MOE_GQA_TARGET 512
+#endif
+constexpr int kAtTarget = MOE_GQA_TARGET;   // workgroups wanted per launch (two per CU)
 
 template <int D>
 struct AttnLds {
-  float q[kAtGroup][D];                 // query rows, fp32
+  uint32_t q[kAtGroup][D / 2];          // query rows, bf16 pairs
   uint16_t k[kAtSub][D + 8];            // key rows; +16 bytes per row: rows start 4 banks apart
   uint16_t v[kAtSub][D];                // value rows
-  float p[kAtGroup][kAtSub];            // exp(score - running max)
+  float p[kAtSub][kAtGroup];            // exp(score - running max), position-major
   float alpha[kAtGroup];                // rescale of the running output for this step
 };
 
@@ -51,13 +55,11 @@ __device__ inline float wave_sum64(float v) {
   return v;
 }
 
-__device__ inline void unpack8(const uint4 w, float* f) {
-  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(u[i] << 16);
-    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-  }
+__device__ inline float dot8(const uint4 a, const uint4 b, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), c, false);
 }
 
 template <int D>
@@ -77,60 +79,70 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
   if (start >= L) return;                         // the merge reads only ranges below L
   const int end = min(start + rows_per_split, L);
 
-  for (int i = tid; i < kAtGroup * D; i += kAtThreads) {
-    const int g = i / D, d = i % D;
-    sm.q[g][d] = g < gw ? bf16_to_f32(q[(static_cast<int64_t>(b) * Hq + h0 + g) * D + d]) : 0.f;
+  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(q);
+  for (int i = tid; i < kAtGroup * (D / 2); i += kAtThreads) {
+    const int g = i / (D / 2), c = i % (D / 2);
+    sm.q[g][c] = g < gw ? q32[((static_cast<int64_t>(b) * Hq + h0 + g) * D) / 2 + c] : 0u;
   }
   const int64_t row0 = (static_cast<int64_t>(b) * Hkv + kv) * S;   // cache row of position 0
   constexpr int kPieces = D / 8;                                     // 16-byte pieces per row
+  constexpr int kLoads = kAtSub * kPieces / kAtThreads;              // per thread and step, each of K and V
 
   // score roles: lane = position within the step, wave w = query slots 2w and 2w + 1
   const int ga = 2 * wave, gb = 2 * wave + 1;
   const bool use_a = ga < gw, use_b = gb < gw;
   float m_a = -INFINITY, m_b = -INFINITY, l_a = 0.f, l_b = 0.f;
 
-  // value roles: thread = (column pair, group of query slots)
-  constexpr int kPairs = D / 2;
-  constexpr int kHg = kAtThreads / kPairs;   // 2, 4 or 8 slot groups
-  constexpr int kHpt = kAtGroup / kHg;       // 4, 2 or 1 slots per thread
-  const int cp = tid % kPairs, hg = tid / kPairs;
-  float acc[kHpt][2];
+  // value roles: lane = (8-column block cb, slot group hgp); wave w takes positions w, w + 4, ...
+  constexpr int kCB = D / 8;
+  constexpr int kHG = 64 / kCB;      // 2, 4 or 8 slot groups
+  constexpr int kHPT = kAtGroup / kHG;   // 4, 2 or 1 slots per lane
+  const int cb = lane % kCB, hgp = lane / kCB;
+  float acc[kHPT][8];
 #pragma unroll
-  for (int j = 0; j < kHpt; ++j) acc[j][0] = acc[j][1] = 0.f;
+  for (int j = 0; j < kHPT; ++j)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[j][c] = 0.f;
+
+  // next step's rows, loaded into registers while the current step computes
+  uint4 kr[kLoads], vr[kLoads];
+  auto load_step = [&](int p0) {
+    const int n = min(kAtSub, end - p0);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = tid + i * kAtThreads;
+      const int r = idx / kPieces, c = idx % kPieces;
+      kr[i] = vr[i] = uint4{0u, 0u, 0u, 0u};
+      if (r < n) {
+        const int64_t off = (row0 + p0 + r) * D + c * 8;
+        kr[i] = *reinterpret_cast<const uint4*>(kc + off);
+        vr[i] = *reinterpret_cast<const uint4*>(vc + off);
+      }
+    }
+  };
+  load_step(start);
 
   for (int p0 = start; p0 < end; p0 += kAtSub) {
     const int n = min(kAtSub, end - p0);
     __syncthreads();   // the previous step's reads of k, v, p and alpha are done
-    for (int i = tid; i < kAtSub * kPieces; i += kAtThreads) {
-      const int r = i / kPieces, c = i % kPieces;
-      uint4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (r < n) {
-        const int64_t off = (row0 + p0 + r) * D + c * 8;
-        kw = *reinterpret_cast<const uint4*>(kc + off);
-        vw = *reinterpret_cast<const uint4*>(vc + off);
-      }
-      *reinterpret_cast<uint4*>(&sm.k[r][c * 8]) = kw;
-      *reinterpret_cast<uint4*>(&sm.v[r][c * 8]) = vw;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = tid + i * kAtThreads;
+      const int r = idx / kPieces, c = idx % kPieces;
+      *reinterpret_cast<uint4*>(&sm.k[r][c * 8]) = kr[i];
+      *reinterpret_cast<uint4*>(&sm.v[r][c * 8]) = vr[i];
     }
     __syncthreads();
+    if (p0 + kAtSub < end) load_step(p0 + kAtSub);
 
     if (use_a) {   // wave-uniform
       float sa = 0.f, sb = 0.f;
-      const uint16_t* kr = &sm.k[lane][0];
+      const uint16_t* krow = &sm.k[lane][0];
 #pragma unroll 4
       for (int d = 0; d < D; d += 8) {
-        float kf[8];
-        unpack8(*reinterpret_cast<const uint4*>(kr + d), kf);
-        const float4 qa0 = *reinterpret_cast<const float4*>(&sm.q[ga][d]);
-        const float4 qa1 = *reinterpret_cast<const float4*>(&sm.q[ga][d + 4]);
-        const float4 qb0 = *reinterpret_cast<const float4*>(&sm.q[gb][d]);
-        const float4 qb1 = *reinterpret_cast<const float4*>(&sm.q[gb][d + 4]);
-        sa = fmaf(qa0.x, kf[0], sa); sa = fmaf(qa0.y, kf[1], sa); sa = fmaf(qa0.z, kf[2], sa);
-        sa = fmaf(qa0.w, kf[3], sa); sa = fmaf(qa1.x, kf[4], sa); sa = fmaf(qa1.y, kf[5], sa);
-        sa = fmaf(qa1.z, kf[6], sa); sa = fmaf(qa1.w, kf[7], sa);
-        sb = fmaf(qb0.x, kf[0], sb); sb = fmaf(qb0.y, kf[1], sb); sb = fmaf(qb0.z, kf[2], sb);
-        sb = fmaf(qb0.w, kf[3], sb); sb = fmaf(qb1.x, kf[4], sb); sb = fmaf(qb1.y, kf[5], sb);
-        sb = fmaf(qb1.z, kf[6], sb); sb = fmaf(qb1.w, kf[7], sb);
+        const uint4 kw = *reinterpret_cast<const uint4*>(krow + d);
+        sa = dot8(*reinterpret_cast<const uint4*>(&sm.q[ga][d / 2]), kw, sa);
+        sb = dot8(*reinterpret_cast<const uint4*>(&sm.q[gb][d / 2]), kw, sb);
       }
       const bool live = lane < n;
       {
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
         const float e = live ? expf(s - mn) : 0.f;
         l_a = l_a * al + wave_sum64(e);
         m_a = mn;
-        sm.p[ga][lane] = e;
+        sm.p[lane][ga] = e;
         if (lane == 0) sm.alpha[ga] = al;
       }
       if (use_b) {
@@ -150,43 +162,62 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
         const float e = live ? expf(s - mn) : 0.f;
         l_b = l_b * al + wave_sum64(e);
         m_b = mn;
-        sm.p[gb][lane] = e;
+        sm.p[lane][gb] = e;
         if (lane == 0) sm.alpha[gb] = al;
       }
     }
     __syncthreads();
 
 #pragma unroll
-    for (int j = 0; j < kHpt; ++j) {
-      const int g = hg * kHpt + j;
-      if (g < gw) {
-        const float al = sm.alpha[g];
-        acc[j][0] *= al;
-        acc[j][1] *= al;
-      }
-    }
-    for (int r = 0; r < n; ++r) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(&sm.v[r][2 * cp]);
-      const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
+    for (int j = 0; j < kHPT; ++j) {
+      const int g = hgp * kHPT + j;
+      const float al = g < gw ? sm.alpha[g] : 0.f;
 #pragma unroll
-      for (int j = 0; j < kHpt; ++j) {
-        const int g = hg * kHpt + j;
-        if (g < gw) {
-          const float pr = sm.p[g][r];
-          acc[j][0] = fmaf(pr, v0, acc[j][0]);
-          acc[j][1] = fmaf(pr, v1, acc[j][1]);
-        }
+      for (int c = 0; c < 8; ++c) acc[j][c] *= al;
+    }
+    for (int r = wave; r < n; r += 4) {
+      float vf[8];
+      const uint4 w = *reinterpret_cast<const uint4*>(&sm.v[r][cb * 8]);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[2 * i] = __uint_as_float(u[i] << 16);
+        vf[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
       }
+      float pr[kHPT];
+      if constexpr (kHPT == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(&sm.p[r][hgp * 4]);
+        pr[0] = t.x; pr[1] = t.y; pr[2] = t.z; pr[3] = t.w;
+      } else if constexpr (kHPT == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(&sm.p[r][hgp * 2]);
+        pr[0] = t.x; pr[1] = t.y;
+      } else {
+        pr[0] = sm.p[r][hgp];
+      }
+#pragma unroll
+      for (int j = 0; j < kHPT; ++j)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[j][c] = fmaf(pr[j], vf[c], acc[j][c]);
     }
   }
 
+  // the four waves' partial sums, added in wave order, through the key area
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&sm.k[0][0]);   // [4][64][kHPT * 8]
+  static_assert(4 * 64 * kHPT * 8 * sizeof(float) <= sizeof(sm.k), "reduction buffer");
 #pragma unroll
-  for (int j = 0; j < kHpt; ++j) {
-    const int g = hg * kHpt + j;
-    if (g < gw) {
-      float* o = part_o + ((static_cast<int64_t>(b) * Hq + h0 + g) * n_splits + split) * D + 2 * cp;
-      *reinterpret_cast<float2*>(o) = make_float2(acc[j][0], acc[j][1]);
-    }
+  for (int j = 0; j < kHPT; ++j)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[(wave * 64 + lane) * (kHPT * 8) + j * 8 + c] = acc[j][c];
+  __syncthreads();
+  for (int o = tid; o < kAtGroup * D; o += kAtThreads) {
+    const int g = o / D, d = o % D;
+    if (g >= gw) continue;
+    const int ln = (g / kHPT) * kCB + d / 8, slot = (g % kHPT) * 8 + d % 8;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sum += red[(w * 64 + ln) * (kHPT * 8) + slot];
+    part_o[((static_cast<int64_t>(b) * Hq + h0 + g) * n_splits + split) * D + d] = sum;
   }
   if (lane == 0) {
     if (use_a) {
@@ -202,25 +233,56 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
   }
 }
 
-// One workgroup per (query head, sequence): the ranges' partial results in
-// range order, out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s, rounded to bf16.
-__global__ __launch_bounds__(kAtThreads) void k_gqa_merge(const float* __restrict__ part_o,
+// One workgroup per (16 output columns, query head, sequence): the ranges'
+// partial results combined as out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Each of 16 split lanes per column adds ranges s = lane, lane + 16, ... in
+// order, and the 16 lane sums are added in lane order, so the result does not
+// depend on scheduling.
+constexpr int kMergeCols = 16;
+__global__ __launch_bounds__(kMgThreads) void k_gqa_merge(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           const int32_t* __restrict__ lens, int Hq, int S, int D,
                                                           int rows_per_split, int n_splits, uint16_t* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y;
+  constexpr int kW = kMgThreads / 64;
+  __shared__ float red[2][kW];
+  __shared__ float part[kMgThreads / kMergeCols][kMergeCols];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * kMergeCols, h = blockIdx.y, b = blockIdx.z;
   const int L = min(max(lens[b], 0), S);
   const int ns = (L + rows_per_split - 1) / rows_per_split;
   const int64_t bh = static_cast<int64_t>(b) * Hq + h;
+  if (ns == 0) {
+    if (tid < kMergeCols) out[bh * D + c0 + tid] = 0;
+    return;
+  }
   const float* ml = part_ml + bh * n_splits * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-  float den = 0.f;
-  for (int s = 0; s < ns; ++s) den = fmaf(expf(ml[2 * s] - M), ml[2 * s + 1], den);
-  for (int d = threadIdx.x; d < D; d += kAtThreads) {
-    float num = 0.f;
-    for (int s = 0; s < ns; ++s) num = fmaf(expf(ml[2 * s] - M), part_o[(bh * n_splits + s) * D + d], num);
-    out[bh * D + d] = ns ? f32_to_bf16_bits(num / den) : static_cast<uint16_t>(0);
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += kMgThreads) mx = fmaxf(mx, ml[2 * s]);
+  mx = wave_max64(mx);
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) M = fmaxf(M, red[0][w]);
+  float dsum = 0.f;
+  for (int s = tid; s < ns; s += kMgThreads) dsum = fmaf(expf(ml[2 * s] - M), ml[2 * s + 1], dsum);
+  dsum = wave_sum64(dsum);
+  if (lane == 0) red[1][wave] = dsum;
+  const int c = tid % kMergeCols, sl = tid / kMergeCols;
+  const float* po = part_o + bh * n_splits * D + c0 + c;
+  float num = 0.f;
+#pragma unroll 4
+  for (int s = sl; s < ns; s += kMgThreads / kMergeCols)
+    num = fmaf(expf(ml[2 * s] - M), po[static_cast<int64_t>(s) * D], num);
+  part[sl][c] = num;
+  __syncthreads();
+  if (tid < kMergeCols) {
+    float den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) den += red[1][w];
+    float t = 0.f;
+    for (int i = 0; i < kMgThreads / kMergeCols; ++i) t += part[i][tid];
+    out[bh * D + c0 + tid] = f32_to_bf16_bits(t / den);
   }
 }
 
@@ -267,8 +329,9 @@ hipError_t launch_gqa_decode(const uint16_t* q, const uint16_t* kc, const uint16
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gqa_merge, dim3(static_cast<unsigned>(Hq), static_cast<unsigned>(B)), dim3(kAtThreads), 0, s,
-                     part_o, part_ml, lens, Hq, S, D, p.rows_per_split, p.n_splits, out);
+  hipLaunchKernelGGL(k_gqa_merge, dim3(static_cast<unsigned>(D / kMergeCols), static_cast<unsigned>(Hq),
+                                      static_cast<unsigned>(B)),
+                     dim3(kMgThreads), 0, s, part_o, part_ml, lens, Hq, S, D, p.rows_per_split, p.n_splits, out);
   return hipGetLastError();
 }
 
