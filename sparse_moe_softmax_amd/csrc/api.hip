@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "internal.hpp"
+#include "attn.hpp"
 
 using namespace moe;
 

@@ -21,6 +21,7 @@
 // head: the unpacked form the packing is measured against.
 
 #include "internal.hpp"
+#include "attn.hpp"
 
 namespace moe {
 
