@@ -27,7 +27,11 @@ namespace moe {
 
 namespace {
 
-constexpr int kAtSub = 64;        // positions staged per step
+#ifndef MOE_GQA_SUB
+#define MOE_GQA_SUB 32
+#endif
+constexpr int kAtSub = MOE_GQA_SUB;   // positions staged per step (64 or 32)
+static_assert(kAtSub == 64 || kAtSub == 32, "step height");
 constexpr int kAtThreads = 256;
 constexpr int kMgThreads = 256;   // merge
 constexpr int kAtGroup = 8;       // query heads per workgroup at most
@@ -136,7 +140,43 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
     __syncthreads();
     if (p0 + kAtSub < end) load_step(p0 + kAtSub);
 
-    if (use_a) {   // wave-uniform
+    if constexpr (kAtSub == 32) {
+      // lane = (position lane % 32, slot 2w + lane / 32): one dot product per lane
+      const int pos = lane & 31, g = 2 * wave + (lane >> 5);
+      if (use_a) {   // wave-uniform
+        float sa = 0.f;
+        const uint16_t* krow = &sm.k[pos][0];
+#pragma unroll 4
+        for (int d = 0; d < D; d += 8)
+          sa = dot8(*reinterpret_cast<const uint4*>(&sm.q[g][d / 2]), *reinterpret_cast<const uint4*>(krow + d), sa);
+        const bool live = pos < n;
+        const float sc = live ? sa * scale : -INFINITY;
+        float mx = sc;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const float mo = (lane >> 5) ? m_b : m_a;
+        const float mn = fmaxf(mo, mx);   // finite: position 0 is live
+        const float al = expf(mo - mn);
+        const float e = live ? expf(sc - mn) : 0.f;
+        float es = e;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) es += __shfl_xor(es, o);
+        // both halves' running values, kept in every lane
+        const float al_a = __shfl(al, 0), al_b = __shfl(al, 32);
+        const float es_a = __shfl(es, 0), es_b = __shfl(es, 32);
+        const float mn_a = __shfl(mn, 0), mn_b = __shfl(mn, 32);
+        l_a = l_a * al_a + es_a;
+        m_a = mn_a;
+        if (use_b) {
+          l_b = l_b * al_b + es_b;
+          m_b = mn_b;
+        }
+        if (g < gw) {
+          sm.p[pos][g] = e;
+          if (pos == 0) sm.alpha[g] = al;
+        }
+      }
+    } else if (use_a) {   // wave-uniform
       float sa = 0.f, sb = 0.f;
       const uint16_t* krow = &sm.k[lane][0];
 #pragma unroll 4
@@ -202,10 +242,10 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
     }
   }
 
-  // the four waves' partial sums, added in wave order, through the key area
+  // the four waves' partial sums, added in wave order, through the key and value area
   __syncthreads();
   float* red = reinterpret_cast<float*>(&sm.k[0][0]);   // [4][64][kHPT * 8]
-  static_assert(4 * 64 * kHPT * 8 * sizeof(float) <= sizeof(sm.k), "reduction buffer");
+  static_assert(4 * 64 * kHPT * 8 * sizeof(float) <= sizeof(sm.k) + sizeof(sm.v), "reduction buffer");
 #pragma unroll
   for (int j = 0; j < kHPT; ++j)
 #pragma unroll
