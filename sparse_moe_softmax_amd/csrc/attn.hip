@@ -297,6 +297,18 @@ __global__ __launch_bounds__(kMgThreads) void k_gqa_merge(const float* __restric
     return;
   }
   const float* ml = part_ml + bh * n_splits * 2;
+  const int c = tid % kMergeCols, sl = tid / kMergeCols;
+  constexpr int kLanes = kMgThreads / kMergeCols;   // split lanes per column
+  const float* po = part_o + bh * n_splits * D + c0 + c;
+  // this lane's first kPre ranges, requested before the maximum is known
+  constexpr int kPre = 16;
+  float ov[kPre], mv[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int s = sl + i * kLanes;
+    ov[i] = s < ns ? po[static_cast<int64_t>(s) * D] : 0.f;
+    mv[i] = s < ns ? ml[2 * s] : -INFINITY;
+  }
   float mx = -INFINITY;
   for (int s = tid; s < ns; s += kMgThreads) mx = fmaxf(mx, ml[2 * s]);
   mx = wave_max64(mx);
@@ -309,11 +321,12 @@ __global__ __launch_bounds__(kMgThreads) void k_gqa_merge(const float* __restric
   for (int s = tid; s < ns; s += kMgThreads) dsum = fmaf(expf(ml[2 * s] - M), ml[2 * s + 1], dsum);
   dsum = wave_sum64(dsum);
   if (lane == 0) red[1][wave] = dsum;
-  const int c = tid % kMergeCols, sl = tid / kMergeCols;
-  const float* po = part_o + bh * n_splits * D + c0 + c;
   float num = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPre; ++i)
+    if (sl + i * kLanes < ns) num = fmaf(expf(mv[i] - M), ov[i], num);
 #pragma unroll 4
-  for (int s = sl; s < ns; s += kMgThreads / kMergeCols)
+  for (int s = sl + kPre * kLanes; s < ns; s += kLanes)
     num = fmaf(expf(ml[2 * s] - M), po[static_cast<int64_t>(s) * D], num);
   part[sl][c] = num;
   __syncthreads();
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(kMgThreads) void k_gqa_merge(const float* __restric
 #pragma unroll
     for (int w = 0; w < kW; ++w) den += red[1][w];
     float t = 0.f;
-    for (int i = 0; i < kMgThreads / kMergeCols; ++i) t += part[i][tid];
+    for (int i = 0; i < kLanes; ++i) t += part[i][tid];
     out[bh * D + c0 + tid] = f32_to_bf16_bits(t / den);
   }
 }
