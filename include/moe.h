@@ -26,10 +26,16 @@
  *   - Row-major layouts; bf16 and fp16 values are passed as uint16_t bit patterns.
  *   - Calls that share a workspace on one stream are ordered; calls that
  *     overlap on different streams must use different workspaces.
+ *   - Every workspace (moe_forward's and moe_group's) starts with a 256-byte
+ *     header whose first int32 is a device error word: kernels OR the
+ *     MOE_DEVERR_* bits into it when they meet a condition that the host could
+ *     not check before launch.  Read and clear it with moe_workspace_errors().
  *
  * Supported shapes: hidden % 64 == 0, inter % 64 == 0, shared_inter % 64 == 0,
  * group_size == 64, n_experts % 16 == 0 and 16 <= n_experts <= 256,
- * 1 <= top_k <= 16 (top_k <= n_experts), 1 <= T <= 65536.
+ * 1 <= top_k <= 16 (top_k <= n_experts), 1 <= T <= 65536.  These cover the
+ * model (256 experts, top-8, groups of 64) with room on every side; wider
+ * expert counts, k up to 32 and other group sizes are MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -48,6 +54,13 @@ typedef enum moe_status {
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   MOE_ERR_HIP = -4          /* a HIP launch failed */
 } moe_status;
+
+/* Bits of the device error word at the start of a workspace. */
+enum {
+  MOE_DEVERR_HANDOVER_TIMEOUT = 1, /* a wait of the fused 1-4-token layer gave up: that call's outputs are invalid */
+  MOE_DEVERR_EXPERT_ID = 2         /* moe_group met an expert id outside [0, E): those slots were skipped, so
+                                      counts, perm and the block map do not cover T*k slots */
+};
 
 /* Layer dimensions.  The workload model uses {2048, 512, 256, 8, 64, 512}. */
 typedef struct moe_dims {
@@ -144,7 +157,13 @@ moe_status moe_router_logits(const moe_dims* d, const moe_layer* layer, const ui
 moe_status moe_route(const moe_dims* d, const float* logits, const float* shared_logit, int32_t T, int32_t* ids,
                      float* weights, float* gate, void* stream);
 
-/* Scratch bytes moe_group() needs for T tokens. */
+/* Device error word of a workspace (moe_forward's or moe_group's): enqueues a
+ * copy of it on `stream`, synchronises the stream, stores the MOE_DEVERR_* bits
+ * in *flags and, when clear != 0, zeroes the word (also stream-ordered and
+ * waited for).  Blocks the calling thread; not for use under graph capture. */
+moe_status moe_workspace_errors(void* workspace, size_t workspace_bytes, int32_t clear, int32_t* flags, void* stream);
+
+/* Scratch bytes moe_group() needs for T tokens (the 256-byte header included). */
 size_t moe_group_workspace_bytes(const moe_dims* d, int32_t T);
 
 /* GPU-resident grouping of the T*k routed slots by expert: histogram and block
@@ -158,52 +177,71 @@ size_t moe_group_workspace_bytes(const moe_dims* d, int32_t T);
  *                     experts ascending; unused entries (-1, -1)
  *   n_tiles  [1]      number of used entries (never leaves the device)
  * max_tiles must be >= moe_max_tiles(T, k, E, block_m); 1 <= block_m <= 4096.
- * ids values must lie in [0, E).  Bitwise deterministic. */
+ * ids values must lie in [0, E): a slot whose id does not is skipped (its
+ * inv_perm entry is -1) and MOE_DEVERR_EXPERT_ID is set in the workspace's
+ * error word.  Bitwise deterministic. */
 moe_status moe_group(const moe_dims* d, const int32_t* ids, int32_t T, int32_t block_m, int32_t* counts,
                      int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* block_map, int32_t max_tiles,
                      int32_t* n_tiles, void* workspace, size_t workspace_bytes, void* stream);
 
 typedef enum moe_epilogue {
-  /* h[p][n] = bf16( silu(gate) * up ), gate/up = a_row . W_gate_up[e]^T, a_row = x[perm[p] / k] */
+  /* h[p][n] = bf16( silu(gate) * up ), gate/up = a_row(p) . W_gate_up[e]^T */
   MOE_EPI_SWIGLU_BF16 = 0,
-  /* y[perm[p] / k][m] += row_weight[perm[p]] * (h[p] . W_down[e]^T)[m]   (fp32 atomics) */
-  MOE_EPI_WEIGHTED_SCATTER_F32 = 1,
-  /* slots[t][j][m] = fp16( row_weight[f] * (h[p] . W_down[e]^T)[m] ), f = perm[p] = t*k + j:
-   * the weighted output of every routed slot, token-major [T][k+1][H] (entry j = k
-   * is the shared expert's and is left untouched).  Summing a token's entries in
-   * order gives the combine without atomics. */
-  MOE_EPI_WEIGHTED_SLOTS_F16 = 2
+  /* y[perm[p] / k][m] += row_weight[perm[p]] * (a_row(p) . W_down[e]^T)[m]   (fp32 atomics) */
+  MOE_EPI_WEIGHTED_SCATTER_F32 = 1
 } moe_epilogue;
 
 /* Grouped GEMM over the tiles of a block map with int4 weights dequantised in
  * registers, tile by tile inside the GEMM (bf16 matrix cores, fp32
  * accumulation; Inside Lily page, section "Performance Gains and Workload
- * Patterns").  Routed experts only.
- *   SWIGLU:  a = x [T][H] bf16 (token rows, gathered through perm);
- *            w = gate_up weights; out = h [T*k][I] bf16 in grouped order.
- *   SCATTER: a = h [T*k][I] bf16 in grouped order; w = down weights;
- *            row_weight [T*k] fp32 indexed by flat slot; out = y [T][H] fp32,
- *            accumulated into (the caller zeroes it first).  Accumulation order
- *            across experts is not fixed, so y is reproducible to fp32 rounding.
- *   SLOTS:   as SCATTER but out = slots [T][k+1][H] fp16 (see MOE_EPI_WEIGHTED_SLOTS_F16);
- *            deterministic.
+ * Patterns"; the weighted scatter-combine is the layer's combine of the k
+ * expert outputs of a token, Lily page, section "The architecture that forces
+ * the issue").  Routed experts only.
+ *   a_row(p): a_rows_are_tokens = 1: row perm[p] / k of a [T][K] (token rows,
+ *             gathered through the permutation); 0: row p of a [T*k][K]
+ *             (rows already in grouped order).  K = H for SWIGLU, I otherwise.
+ *   SWIGLU:  w = gate_up weights; out = h [T*k][I] bf16 in grouped order.
+ *   SCATTER: w = down weights; row_weight [T*k] fp32 indexed by flat slot;
+ *            out = y [T][H] fp32, accumulated into (the caller zeroes it
+ *            first).  Accumulation order across experts is not fixed, so y is
+ *            reproducible to fp32 rounding.
  * w->packed must hold the matrix-core layout of the routed experts' matrix
- * (MOE_MAT_GATE_UP for SWIGLU, MOE_MAT_DOWN otherwise).
+ * (MOE_MAT_GATE_UP for SWIGLU, MOE_MAT_DOWN otherwise): the grouped GEMMs read
+ * only that layout (moe_prepack_q4), never the canonical arrays.
  * perm/offsets/block_map/n_tiles as produced by moe_group() with the same
- * block_m; 1 <= block_m <= moe_block_m(). */
+ * block_m (the kernels trust them: expert ids in [0, E), rows inside [0, T*k));
+ * 1 <= block_m <= moe_block_m(). */
 moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
-                               const int32_t* perm, const int32_t* offsets, const int32_t* block_map,
-                               const int32_t* n_tiles, int32_t max_tiles, const float* row_weight, int32_t T,
-                               int32_t block_m, void* out, void* stream);
+                               int32_t a_rows_are_tokens, const int32_t* perm, const int32_t* offsets,
+                               const int32_t* block_map, const int32_t* n_tiles, int32_t max_tiles,
+                               const float* row_weight, int32_t T, int32_t block_m, void* out, void* stream);
 
-/* Scratch bytes moe_forward() needs for up to T_max tokens.  The workspace
- * starts with the hand-over words of the fused path (1-4 tokens): per-block
- * counts of completed calls and tagged data words.  They must be zero before a
- * workspace's first fused call (allocate it zero-filled); after that every
- * fused call keeps them consistent, and the grouped path never writes them. */
+/* Scratch bytes moe_forward() needs for up to T_max tokens.  After the
+ * 256-byte header (error word) come the hand-over words of the fused path (1-4
+ * tokens): per-block counts of completed calls and tagged data words.  They
+ * must be zero before a workspace's first fused call (allocate it
+ * zero-filled); after that every fused call keeps them consistent, and the
+ * grouped path never writes them. */
 size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
 
-/* The whole layer for T tokens:
+/* The fused layer that moe_forward runs for T tokens of these dims (T <= 4,
+ * see moe_forward) launches *needed workgroups that hand data to each other,
+ * so all of them must be resident on the device at once.  *resident is what
+ * the current device holds of that kernel at once (compute units x workgroups
+ * per unit).  moe_forward refuses the fused path with MOE_ERR_UNSUPPORTED when
+ * resident < needed (a partitioned or CU-masked device).  Returns
+ * MOE_ERR_UNSUPPORTED when (d, T) does not take the fused path and MOE_ERR_HIP
+ * when the device cannot be queried.  The answer is kept per device. */
+moe_status moe_fused_residency(const moe_dims* d, int32_t T, int32_t* needed, int32_t* resident);
+
+/* The whole layer for T tokens: every token is scored against the routed
+ * experts, the best k are kept and a shared expert runs on every token (Lily
+ * page, section "The architecture that forces the issue: MoE plus Gated
+ * DeltaNet"); routing histograms and block maps stay on the GPU and the int4
+ * weights are rebuilt inside the grouped GEMMs (Inside Lily page, section
+ * "Performance Gains and Workload Patterns"); one token runs as GEMV on the
+ * vector ALUs (Lily page, section "Why Apple Silicon isn't just a smaller
+ * datacenter GPU"):
  *   y[t] = bf16( sum_j w[t][j] * E_{ids[t][j]}(x[t]) + g[t] * E_shared(x[t]) ),
  *   E(x) = ( silu(x.Wg^T) * (x.Wu^T) ) . Wd^T with the SwiGLU product rounded to bf16.
  * T == 1 (and 2 <= T <= 4 with hidden <= 2048, inter and shared_inter <= 512,
@@ -215,10 +253,13 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max);
  * the matrix cores (needs router_w3 and the packed weights of all four
  * matrices) and the combine;
  * the shared expert's tiles run in the same GEMM launches.  The down GEMM stores every
- * routed slot's output and the shared expert's output in fp16, unweighted, and
- * a final pass multiplies each of a token's k+1 entries by its routing weight
- * (the shared one by the gate) and sums them in slot order in fp32, so y is
- * bitwise reproducible.
+ * routed slot's output and the shared expert's output unweighted, as fp16
+ * values with a power-of-two exponent per 64 columns (fp32's range; fp16's
+ * 11-bit precision for every value within 2^24 of its 64-column chunk's
+ * largest), and a final pass multiplies each of a token's k+1 entries by its
+ * routing weight (the shared one by the gate) and sums them in slot order in
+ * fp32, so y is bitwise reproducible.  The fused path keeps everything in
+ * fp32 registers.  Inputs must be finite.
  * No host synchronisation anywhere.
  * Optional outputs (NULL to skip): logits_out [T][E], ids_out [T][k], w_out [T][k].
  * workspace_bytes must be >= moe_workspace_bytes(d, T). */

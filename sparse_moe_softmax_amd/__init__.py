@@ -21,16 +21,17 @@ __all__ = [
     "moe_router_logits", "moe_route", "moe_group_workspace_bytes", "moe_group", "moe_grouped_gemm_q4",
     "moe_workspace_bytes", "moe_workspace", "moe_forward", "moe_forward_stages", "moe_packed_q4_bytes",
     "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes", "moe_forward_host_routing",
-    "moe_gqa_decode_workspace_bytes", "moe_gqa_decode_attention",
-    "MOE_EPI_SWIGLU_BF16",
-    "MOE_EPI_WEIGHTED_SCATTER_F32", "STAGES",
-    "EXPORTED_SYMBOLS",
+    "moe_gqa_decode_workspace_bytes", "moe_gqa_decode_attention", "moe_workspace_errors", "moe_fused_residency",
+    "MOE_EPI_SWIGLU_BF16", "MOE_EPI_WEIGHTED_SCATTER_F32", "MOE_DEVERR_HANDOVER_TIMEOUT", "MOE_DEVERR_EXPERT_ID",
+    "STAGES", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
-MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32, MOE_EPI_WEIGHTED_SLOTS_F16 = 0, 1, 2
+MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32 = 0, 1
+MOE_DEVERR_HANDOVER_TIMEOUT, MOE_DEVERR_EXPERT_ID = 1, 2
+WORKSPACE_HEADER_BYTES = 256   # the device error word is the first int32
 STAGES = ("router", "topk", "group", "gate_up", "down", "combine")  # MOE_STAGE_* in order
 MOE_MAT_GATE_UP, MOE_MAT_DOWN, MOE_MAT_SH_GATE_UP, MOE_MAT_SH_DOWN = 0, 1, 2, 3
 
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "moe_forward_stages", "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
     "moe_packed_q4_bytes", "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes",
     "moe_forward_host_routing", "moe_gqa_decode_workspace_bytes", "moe_gqa_decode_attention",
+    "moe_workspace_errors", "moe_fused_residency",
 )
 
 
@@ -94,8 +96,8 @@ def lib():
             "moe_route": ([PD, _P, _P, _I32, _P, _P, _P, _P], _I32),
             "moe_group_workspace_bytes": ([PD, _I32], _SZ),
             "moe_group": ([PD, _P, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P], _I32),
-            "moe_grouped_gemm_q4": ([PD, ctypes.POINTER(_Q4), _I32, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P],
-                                    _I32),
+            "moe_grouped_gemm_q4": ([PD, ctypes.POINTER(_Q4), _I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                     _P, _P], _I32),
             "moe_workspace_bytes": ([PD, _I32], _SZ),
             "moe_forward": ([PD, PL, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P], _I32),
             "moe_forward_stages": ([PD, PL, _P, _I32, _P, _P, _P, _P, _P, _SZ, _I32, _I32, _P], _I32),
@@ -110,6 +112,8 @@ def lib():
             "moe_gqa_decode_workspace_bytes": ([_I32] * 5, _SZ),
             "moe_gqa_decode_attention": ([_P, _P, _P, _P] + [_I32] * 5 + [ctypes.c_float, _I32, _P, _P, _SZ, _P],
                                          _I32),
+            "moe_workspace_errors": ([_P, _SZ, _I32, ctypes.POINTER(_I32), _P], _I32),
+            "moe_fused_residency": ([PD, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], _I32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(h, name)
@@ -259,16 +263,37 @@ def moe_group(d, ids: torch.Tensor, block_m: int, max_tiles: int | None = None, 
 
 
 def moe_grouped_gemm_q4(d, w, epi: int, a: torch.Tensor, perm, offsets, block_map, n_tiles, max_tiles: int,
-                        row_weight, T: int, block_m: int, out: torch.Tensor):
+                        row_weight, T: int, block_m: int, out: torch.Tensor, a_rows_are_tokens: bool | None = None):
+    """a_rows_are_tokens: rows of ``a`` are tokens, gathered through perm (the
+    default for SWIGLU), or already in grouped order (the default for SCATTER)."""
+    if a_rows_are_tokens is None:
+        a_rows_are_tokens = epi == MOE_EPI_SWIGLU_BF16
     q = _q4(w)
-    _check(lib().moe_grouped_gemm_q4(ctypes.byref(_dims(d)), ctypes.byref(q), epi, _ptr(a), _ptr(perm),
-                                     _ptr(offsets), _ptr(block_map), _ptr(n_tiles), max_tiles, _ptr(row_weight), T,
-                                     block_m, _ptr(out), _stream()))
+    _check(lib().moe_grouped_gemm_q4(ctypes.byref(_dims(d)), ctypes.byref(q), epi, _ptr(a),
+                                     1 if a_rows_are_tokens else 0, _ptr(perm), _ptr(offsets), _ptr(block_map),
+                                     _ptr(n_tiles), max_tiles, _ptr(row_weight), T, block_m, _ptr(out), _stream()))
     return out
 
 
 def moe_workspace_bytes(d, T_max: int) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(_dims(d)), T_max))
+
+
+def moe_workspace_errors(workspace: torch.Tensor, clear: bool = False) -> int:
+    """The MOE_DEVERR_* bits of a workspace's device error word (synchronises
+    the current stream); clear=True zeroes the word afterwards."""
+    flags = ctypes.c_int32(0)
+    _check(lib().moe_workspace_errors(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      1 if clear else 0, ctypes.byref(flags), _stream()))
+    return int(flags.value)
+
+
+def moe_fused_residency(d, T: int):
+    """(workgroups the fused layer for T tokens launches, workgroups of it the
+    current device holds at once)."""
+    n, r = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().moe_fused_residency(ctypes.byref(_dims(d)), T, ctypes.byref(n), ctypes.byref(r)))
+    return int(n.value), int(r.value)
 
 
 def moe_workspace(d, T_max: int, device="cuda") -> torch.Tensor:

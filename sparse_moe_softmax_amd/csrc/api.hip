@@ -3,6 +3,9 @@
 // device and nothing allocates device memory.
 #include <algorithm>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -72,10 +75,13 @@ moe_status check_gemm_extent(const moe_dims& d, int32_t T) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Every workspace starts with this header; its first word is the device error word.
+constexpr size_t kWsHeader = 256;
+
 // Workspace regions of moe_forward.
 struct Ws {
-  size_t sync, logits, s, rparts, sparts, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, trows, ntiles, h, hsh,
-      slots;
+  size_t sync, logits, s, rparts, sparts, ids, wts, gate, tilehist, tilebase, counts, offsets, perm, inv, bmap, trows,
+      ntiles, h, hsh, slots, sexp;
   int splits;
   size_t total;
 };
@@ -92,7 +98,8 @@ Ws layout(const moe_dims& d, int32_t T) {
     o = align256(o + bytes);
     return at;
   };
-  w.sync = take(decode_sync_bytes(d));   // fused-path hand-over words: first, never written by the grouped path
+  take(kWsHeader);                       // error word
+  w.sync = take(decode_sync_bytes(d));   // fused-path hand-over words, never written by the grouped path
   w.logits = take(T * E * 4);
   w.s = take(T * 4);
   w.splits = T > 1 ? router_splits(T, d.hidden, d.n_experts) : 1;
@@ -113,6 +120,7 @@ Ws layout(const moe_dims& d, int32_t T) {
   w.h = take(F * I * 2);
   w.hsh = take(static_cast<size_t>(T) * Is * 2);
   w.slots = take(static_cast<size_t>(T) * (k + 1) * H * 2);
+  w.sexp = take(static_cast<size_t>(T) * (k + 1) * (H / 64));
   w.total = o;
   return w;
 }
@@ -121,6 +129,34 @@ template <class T>
 T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
+
+// Residency of the fused layer's kernel on the current device, queried once
+// per (device, dims, T) and kept.
+std::mutex g_res_mu;
+std::map<std::tuple<int, int, int, int, int, int, int>, std::pair<int, int>> g_res;
+
+hipError_t fused_residency(const moe_dims& d, int T, int* needed, int* resident) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_tuple(dev, d.hidden, d.inter, d.shared_inter, d.n_experts, d.top_k, T);
+  {
+    std::lock_guard<std::mutex> lk(g_res_mu);
+    auto it = g_res.find(key);
+    if (it != g_res.end()) {
+      *needed = it->second.first;
+      *resident = it->second.second;
+      return hipSuccess;
+    }
+  }
+  e = decode_residency(d, T, needed, resident);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_res_mu);
+  g_res[key] = {*needed, *resident};
+  return hipSuccess;
+}
+
+__global__ void k_clear_word(uint32_t* w) { *w = 0u; }
 
 }  // namespace
 
@@ -211,7 +247,7 @@ moe_status moe_prepack_q4(const moe_dims* d, int32_t matrix, const moe_q4* w, in
 size_t moe_group_workspace_bytes(const moe_dims* d, int32_t T) {
   if (check_dims(d) || check_T(T)) return 0;
   const size_t ntile = static_cast<size_t>(div_up(T, kTopkTile));
-  return 2 * align256(ntile * d->n_experts * 4);
+  return kWsHeader + 2 * align256(ntile * d->n_experts * 4);
 }
 
 moe_status moe_group(const moe_dims* d, const int32_t* ids, int32_t T, int32_t block_m, int32_t* counts,
@@ -230,18 +266,20 @@ moe_status moe_group(const moe_dims* d, const int32_t* ids, int32_t T, int32_t b
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t ntile = static_cast<size_t>(div_up(T, kTopkTile));
-  int32_t* tilehist = at<int32_t>(workspace, 0);
-  int32_t* tilebase = at<int32_t>(workspace, align256(ntile * d->n_experts * 4));
-  if ((st = hip_check(launch_tile_hist(ids, T, d->top_k, d->n_experts, tilehist, s), "tile histogram"))) return st;
+  uint32_t* err = at<uint32_t>(workspace, 0);
+  int32_t* tilehist = at<int32_t>(workspace, kWsHeader);
+  int32_t* tilebase = at<int32_t>(workspace, kWsHeader + align256(ntile * d->n_experts * 4));
+  if ((st = hip_check(launch_tile_hist(ids, T, d->top_k, d->n_experts, tilehist, err, s), "tile histogram")))
+    return st;
   return hip_check(launch_group(ids, tilehist, tilebase, T, d->top_k, d->n_experts, block_m, counts, offsets, perm,
-                                inv_perm, block_map, max_tiles, n_tiles, nullptr, s),
+                                inv_perm, block_map, max_tiles, n_tiles, nullptr, err, s),
                    "grouping");
 }
 
 moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
-                               const int32_t* perm, const int32_t* offsets, const int32_t* block_map,
-                               const int32_t* n_tiles, int32_t max_tiles, const float* row_weight, int32_t T,
-                               int32_t block_m, void* out, void* stream) {
+                               int32_t a_rows_are_tokens, const int32_t* perm, const int32_t* offsets,
+                               const int32_t* block_map, const int32_t* n_tiles, int32_t max_tiles,
+                               const float* row_weight, int32_t T, int32_t block_m, void* out, void* stream) {
   moe_status st = check_dims(d);
   if (st) return st;
   if ((st = check_T(T))) return st;
@@ -250,22 +288,25 @@ moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue 
   if (!a || !perm || !offsets || !block_map || !n_tiles || !out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
   if (block_m < 1 || block_m > kBM) return fail(MOE_ERR_INVALID_ARG, "block_m=%d outside [1, %d]", block_m, kBM);
   if (max_tiles < 1) return fail(MOE_ERR_INVALID_ARG, "max_tiles must be positive");
-  GemmTiles tl{perm, offsets, block_map, n_tiles, max_tiles, block_m, 0};
+  if (a_rows_are_tokens != 0 && a_rows_are_tokens != 1)
+    return fail(MOE_ERR_INVALID_ARG, "a_rows_are_tokens must be 0 or 1");
+  const bool gather = a_rows_are_tokens == 1;
+  {
+    // rows of `a` are addressed with 32-bit byte offsets
+    const int64_t rows = gather ? T : static_cast<int64_t>(T) * d->top_k;
+    const int64_t K = epi == MOE_EPI_SWIGLU_BF16 ? d->hidden : d->inter;
+    if (rows * K * 2 >= (int64_t{1} << 32)) return fail(MOE_ERR_UNSUPPORTED, "a: 4 GiB or more");
+  }
+  GemmTiles tl{perm, offsets, block_map, n_tiles, max_tiles, block_m, 0, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (epi == MOE_EPI_SWIGLU_BF16)
-    return hip_check(launch_gemm_swiglu(*d, *w, nullptr, a, tl, T, static_cast<uint16_t*>(out), nullptr, s),
+    return hip_check(launch_gemm_swiglu(*d, *w, nullptr, a, gather, tl, T, static_cast<uint16_t*>(out), nullptr, s),
                      "grouped gemm (swiglu)");
   if (epi == MOE_EPI_WEIGHTED_SCATTER_F32) {
     if (!row_weight) return fail(MOE_ERR_INVALID_ARG, "row_weight is NULL");
-    return hip_check(
-        launch_gemm_scatter(*d, *w, nullptr, a, nullptr, tl, row_weight, nullptr, T, static_cast<float*>(out), s),
-        "grouped gemm (scatter)");
-  }
-  if (epi == MOE_EPI_WEIGHTED_SLOTS_F16) {
-    if (!row_weight) return fail(MOE_ERR_INVALID_ARG, "row_weight is NULL");
-    return hip_check(
-        launch_gemm_slots(*d, *w, nullptr, a, nullptr, tl, row_weight, nullptr, T, static_cast<uint16_t*>(out), s),
-        "grouped gemm (slots)");
+    return hip_check(launch_gemm_scatter(*d, *w, nullptr, a, gather, nullptr, tl, row_weight, nullptr, T,
+                                         static_cast<float*>(out), s),
+                     "grouped gemm (scatter)");
   }
   return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", static_cast<int>(epi));
 }
@@ -308,13 +349,21 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
   float* gate = at<float>(workspace, w.gate);
   auto run = [&](int stage) { return first <= stage && stage <= last; };
 
+  uint32_t* err = at<uint32_t>(workspace, 0);
   if (fused) {
-    // one launch for the whole layer, run as the ROUTER stage
-    DecodePtrs p{logits, s_logit, ids, wts, gate, at<void>(workspace, w.sync)};
+    // one launch for the whole layer, run as the ROUTER stage; its workgroups
+    // wait for each other, so all of them must be resident at once
+    int needed = 0, resident = 0;
+    if ((st = hip_check(fused_residency(*d, T, &needed, &resident), "device query"))) return st;
+    if (resident < needed)
+      return fail(MOE_ERR_UNSUPPORTED, "the fused layer needs %d co-resident workgroups; the device holds %d", needed,
+                  resident);
+    DecodePtrs p{logits, s_logit, ids, wts, gate, at<void>(workspace, w.sync), err};
     if (run(MOE_STAGE_ROUTER)) return hip_check(launch_decode_layer(*d, *L, x, T, y, p, s), "fused layer");
     return MOE_OK;
   }
   uint16_t* slots = at<uint16_t>(workspace, w.slots);
+  uint8_t* sexp = at<uint8_t>(workspace, w.sexp);
   int32_t* tilehist = at<int32_t>(workspace, w.tilehist);
   int32_t* counts = at<int32_t>(workspace, w.counts);
   int32_t* offsets = at<int32_t>(workspace, w.offsets);
@@ -347,19 +396,19 @@ moe_status moe_forward_stages(const moe_dims* d, const moe_layer* L, const uint1
     return st;
   if (run(MOE_STAGE_GROUP) &&
       (st = hip_check(launch_group(ids, tilehist, at<int32_t>(workspace, w.tilebase), T, k, E, kBM, counts, offsets,
-                                   perm, at<int32_t>(workspace, w.inv), bmap, mt, ntiles, trows, s),
+                                   perm, at<int32_t>(workspace, w.inv), bmap, mt, ntiles, trows, err, s),
                       "grouping")))
     return st;
   if (run(MOE_STAGE_GATE_UP) &&
-      (st = hip_check(launch_gemm_swiglu(*d, L->gate_up, &L->sh_gate_up, x, tl, T, h, hsh, s), "gate/up gemm")))
+      (st = hip_check(launch_gemm_swiglu(*d, L->gate_up, &L->sh_gate_up, x, true, tl, T, h, hsh, s),
+                      "gate/up gemm")))
     return st;
   // slots are stored unweighted; the combine applies routing weights and the gate
   if (run(MOE_STAGE_DOWN) &&
-      (st = hip_check(launch_gemm_slots(*d, L->down, &L->sh_down, h, hsh, tl, nullptr, nullptr, T, slots, s),
-                      "down gemm")))
+      (st = hip_check(launch_gemm_slots(*d, L->down, &L->sh_down, h, hsh, tl, T, slots, sexp, s), "down gemm")))
     return st;
   if (run(MOE_STAGE_COMBINE) &&
-      (st = hip_check(launch_combine(slots, wts, gate, y, T, d->hidden, k, s), "combine")))
+      (st = hip_check(launch_combine(slots, sexp, wts, gate, y, T, d->hidden, k, s), "combine")))
     return st;
   return MOE_OK;
 }
@@ -446,11 +495,49 @@ moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* L, const
       (st = hip_check(hipMemcpyAsync(ntiles, h_ntiles, 4, hipMemcpyHostToDevice, s), "n_tiles")) ||
       (st = hip_check(launch_group_scatter(ids, counts, tilebase, T, k, E, kBM, offsets,
                                            at<int32_t>(workspace, w.perm), at<int32_t>(workspace, w.inv), bmap, mt,
-                                           ntiles, false, at<int32_t>(workspace, w.trows), s),
+                                           ntiles, false, at<int32_t>(workspace, w.trows),
+                                           at<uint32_t>(workspace, 0), s),
                       "permutation")))
     return st;
   return moe_forward_stages(d, L, x, T, y, nullptr, ids_out, w_out, workspace, workspace_bytes, MOE_STAGE_GATE_UP,
                             MOE_STAGE_COMBINE, stream);
+}
+
+moe_status moe_fused_residency(const moe_dims* d, int32_t T, int32_t* needed, int32_t* resident) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  if (!needed || !resident) return fail(MOE_ERR_INVALID_ARG, "NULL output pointer");
+  *needed = 0;
+  *resident = 0;
+  if (!(T <= kDecMaxT && decode_supported(*d, T)))
+    return fail(MOE_ERR_UNSUPPORTED, "T=%d does not run the fused layer for these dims", T);
+  int n = 0, r = 0;
+  if ((st = hip_check(fused_residency(*d, T, &n, &r), "device query"))) return st;
+  *needed = n;
+  *resident = r;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_errors(void* workspace, size_t workspace_bytes, int32_t clear, int32_t* flags,
+                                void* stream) {
+  if (!workspace || workspace_bytes < kWsHeader) return fail(MOE_ERR_WORKSPACE, "workspace missing or too small");
+  if (!flags) return fail(MOE_ERR_INVALID_ARG, "flags is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* word = at<uint32_t>(workspace, 0);
+  uint32_t v = 0;
+  moe_status st;
+  if ((st = hip_check(hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, s), "error word to host")) ||
+      (st = hip_check(hipStreamSynchronize(s), "stream synchronize")))
+    return st;
+  *flags = static_cast<int32_t>(v);
+  if (clear) {
+    hipLaunchKernelGGL(k_clear_word, dim3(1), dim3(1), 0, s, word);
+    if ((st = hip_check(hipGetLastError(), "clear error word")) ||
+        (st = hip_check(hipStreamSynchronize(s), "stream synchronize")))
+      return st;
+  }
+  return MOE_OK;
 }
 
 // ------------------------------------------------------------------ grouped-query decode attention

@@ -10,11 +10,13 @@
 // instead of loading it once per query head.
 //
 // Here one workgroup owns (sequence, key/value head, range of positions) and
-// all the group's query heads (at most 8).  It stages 64 key and value rows at
-// a time in LDS with 16-byte loads, scores every staged row against every
-// query head (lane = position, wave = two heads), keeps a running maximum and
-// sum per head (online softmax), and accumulates the weighted value rows in
-// fp32 registers.  Each range leaves its (maximum, sum, unnormalised output) in
+// all the group's query heads (at most 8).  It stages 32 key and value rows at
+// a time in LDS with 16-byte loads (the next 32 rows are loaded into registers
+// meanwhile), scores every staged row against every query head (lane =
+// (position, one of the wave's two heads): one dot product per lane), keeps a
+// running maximum and sum per head (online softmax), and accumulates the
+// weighted value rows in fp32 registers (lane = 8 columns x a group of heads;
+// the four waves take every fourth position and are added at the end).  Each range leaves its (maximum, sum, unnormalised output) in
 // the workspace; k_gqa_merge combines a head's ranges in range order, so the
 // result does not depend on scheduling.  With one query head per workgroup
 // (pack_heads == 0) the same kernel reads each key/value row once per query
@@ -27,18 +29,11 @@ namespace moe {
 
 namespace {
 
-#ifndef MOE_GQA_SUB
-#define MOE_GQA_SUB 32
-#endif
-constexpr int kAtSub = MOE_GQA_SUB;   // positions staged per step (64 or 32)
-static_assert(kAtSub == 64 || kAtSub == 32, "step height");
+constexpr int kAtSub = 32;        // positions staged per step: one per lane of a half wave
 constexpr int kAtThreads = 256;
 constexpr int kMgThreads = 256;   // merge
 constexpr int kAtGroup = 8;       // query heads per workgroup at most
-#ifndef MOE_GQA_TARGET
-#define MOE_GQA_TARGET 512
-#endif
-constexpr int kAtTarget = MOE_GQA_TARGET;   // workgroups wanted per launch (two per CU)
+constexpr int kAtTarget = 512;    // workgroups wanted per launch (three fit a CU: 38 KB LDS, 148 VGPRs)
 
 template <int D>
 struct AttnLds {
@@ -140,71 +135,39 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
     __syncthreads();
     if (p0 + kAtSub < end) load_step(p0 + kAtSub);
 
-    if constexpr (kAtSub == 32) {
-      // lane = (position lane % 32, slot 2w + lane / 32): one dot product per lane
-      const int pos = lane & 31, g = 2 * wave + (lane >> 5);
-      if (use_a) {   // wave-uniform
-        float sa = 0.f;
-        const uint16_t* krow = &sm.k[pos][0];
+    // lane = (position lane % 32, slot 2w + lane / 32): one dot product per lane
+    const int pos = lane & 31, g = 2 * wave + (lane >> 5);
+    if (use_a) {   // wave-uniform
+      float sa = 0.f;
+      const uint16_t* krow = &sm.k[pos][0];
 #pragma unroll 4
-        for (int d = 0; d < D; d += 8)
-          sa = dot8(*reinterpret_cast<const uint4*>(&sm.q[g][d / 2]), *reinterpret_cast<const uint4*>(krow + d), sa);
-        const bool live = pos < n;
-        const float sc = live ? sa * scale : -INFINITY;
-        float mx = sc;
+      for (int d = 0; d < D; d += 8)
+        sa = dot8(*reinterpret_cast<const uint4*>(&sm.q[g][d / 2]), *reinterpret_cast<const uint4*>(krow + d), sa);
+      const bool live = pos < n;
+      const float sc = live ? sa * scale : -INFINITY;
+      float mx = sc;
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        const float mo = (lane >> 5) ? m_b : m_a;
-        const float mn = fmaxf(mo, mx);   // finite: position 0 is live
-        const float al = expf(mo - mn);
-        const float e = live ? expf(sc - mn) : 0.f;
-        float es = e;
+      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float mo = (lane >> 5) ? m_b : m_a;
+      const float mn = fmaxf(mo, mx);   // finite: position 0 is live
+      const float al = expf(mo - mn);
+      const float e = live ? expf(sc - mn) : 0.f;
+      float es = e;
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) es += __shfl_xor(es, o);
-        // both halves' running values, kept in every lane
-        const float al_a = __shfl(al, 0), al_b = __shfl(al, 32);
-        const float es_a = __shfl(es, 0), es_b = __shfl(es, 32);
-        const float mn_a = __shfl(mn, 0), mn_b = __shfl(mn, 32);
-        l_a = l_a * al_a + es_a;
-        m_a = mn_a;
-        if (use_b) {
-          l_b = l_b * al_b + es_b;
-          m_b = mn_b;
-        }
-        if (g < gw) {
-          sm.p[pos][g] = e;
-          if (pos == 0) sm.alpha[g] = al;
-        }
-      }
-    } else if (use_a) {   // wave-uniform
-      float sa = 0.f, sb = 0.f;
-      const uint16_t* krow = &sm.k[lane][0];
-#pragma unroll 4
-      for (int d = 0; d < D; d += 8) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(krow + d);
-        sa = dot8(*reinterpret_cast<const uint4*>(&sm.q[ga][d / 2]), kw, sa);
-        sb = dot8(*reinterpret_cast<const uint4*>(&sm.q[gb][d / 2]), kw, sb);
-      }
-      const bool live = lane < n;
-      {
-        const float s = live ? sa * scale : -INFINITY;
-        const float mn = fmaxf(m_a, wave_max64(s));   // finite: lane 0 is live
-        const float al = expf(m_a - mn);
-        const float e = live ? expf(s - mn) : 0.f;
-        l_a = l_a * al + wave_sum64(e);
-        m_a = mn;
-        sm.p[lane][ga] = e;
-        if (lane == 0) sm.alpha[ga] = al;
-      }
+      for (int o = 16; o > 0; o >>= 1) es += __shfl_xor(es, o);
+      // both halves' running values, kept in every lane
+      const float al_a = __shfl(al, 0), al_b = __shfl(al, 32);
+      const float es_a = __shfl(es, 0), es_b = __shfl(es, 32);
+      const float mn_a = __shfl(mn, 0), mn_b = __shfl(mn, 32);
+      l_a = l_a * al_a + es_a;
+      m_a = mn_a;
       if (use_b) {
-        const float s = live ? sb * scale : -INFINITY;
-        const float mn = fmaxf(m_b, wave_max64(s));
-        const float al = expf(m_b - mn);
-        const float e = live ? expf(s - mn) : 0.f;
-        l_b = l_b * al + wave_sum64(e);
-        m_b = mn;
-        sm.p[lane][gb] = e;
-        if (lane == 0) sm.alpha[gb] = al;
+        l_b = l_b * al_b + es_b;
+        m_b = mn_b;
+      }
+      if (g < gw) {
+        sm.p[pos][g] = e;
+        if (pos == 0) sm.alpha[g] = al;
       }
     }
     __syncthreads();

@@ -36,8 +36,10 @@
 // keeps the number of calls it has completed in its own word of the
 // workspace; all blocks finish every call, so they agree on it.  The
 // workgroups of one launch are all resident (kDecBlocks <= CUs, one block fits
-// a CU), so every wait ends; a wait that exceeds kSpinLimit polls sets the
-// timeout word and carries on, so a launch always completes.
+// a CU; the host checks the device's residency before it launches), so every
+// wait ends; a wait that exceeds kSpinLimit polls sets the hand-over timeout
+// bit of the workspace's error word and carries on, so a launch always
+// completes.
 #include "gemv.hpp"
 #include "topk.hpp"
 
@@ -51,8 +53,7 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // Workspace words of the fused path (zero before the first call).
 struct DecSync {
   uint32_t gen[kDecBlocks];   // calls completed, per block
-  uint32_t timeout;
-  uint32_t pad[63];
+  uint32_t pad[64];
   uint64_t words[1];          // logit words [T][E + 1], then h words [T][k + 1][ldh / 2]
 };
 
@@ -71,6 +72,7 @@ struct DecArgs {
   int ldh;                 // h row stride (multiple of 8)
   uint16_t* y;             // [T][H] bf16
   DecSync* sync;
+  uint32_t* err;           // the workspace's device error word
 };
 
 template <class T>
@@ -94,7 +96,7 @@ __device__ inline uint64_t tagged(uint32_t tag, uint32_t payload) {
 // r + 2's write before every wave has passed round r + 1's barrier, that is,
 // has read round r's verdicts).
 template <int M, int C, class Live>
-__device__ inline void poll_words(const uint64_t* words, int n, uint32_t tag, uint32_t* out, uint32_t* timeout,
+__device__ inline void poll_words(const uint64_t* words, int n, uint32_t tag, uint32_t* out, uint32_t* err,
                                   Live live, uint32_t (&done)[2][kDecWaves]) {
   const int tid = threadIdx.x;
   uint32_t pending = 0;
@@ -125,7 +127,9 @@ __device__ inline void poll_words(const uint64_t* words, int n, uint32_t tag, ui
     for (int w = 0; w < kDecWaves; ++w) all &= done[it & 1u][w];
     if (all) return;
     if (it >= kSpinLimit) {
-      if (tid == 0) put(timeout, 1u);
+      if (tid == 0)
+        __hip_atomic_fetch_or(err, static_cast<uint32_t>(MOE_DEVERR_HANDOVER_TIMEOUT), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -318,7 +322,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
 
   // ---- D: routing decision of every token (every block)
   poll_words<(TM * (kDecMaxE + 1) + kDecThreads - 1) / kDecThreads, (TM * (kDecMaxE + 1) + kDecThreads - 1) / kDecThreads>(
-      lw, T * (E + 1), tag, &s_l[0][0], &sy->timeout, [](int) { return true; }, s_done);
+      lw, T * (E + 1), tag, &s_l[0][0], a.err, [](int) { return true; }, s_done);
   if constexpr (TM > 1) {
     // the polled words are [T][E + 1]; the rows of s_l are kDecMaxE + 1 apart
     for (int t = T - 1; t > 0; --t) {
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
   // registers to spare: there one word is requested at a time)
   constexpr int kHChunk = KCG * KCD == 4 && KMAX > 8 ? 1 : (kHPerThread < 9 ? kHPerThread : 9);
   poll_words<kHPerThread, kHChunk>(
-      hw, T * (k + 1) * hp, tag, hs32, &sy->timeout,
+      hw, T * (k + 1) * hp, tag, hs32, a.err,
       [&](int i) {
         const int slot = i / hp;
         const int j = slot % (k + 1);
@@ -508,11 +512,40 @@ size_t decode_sync_bytes(const moe_dims& d) {
 }
 
 template <int KCG, int KCD>
-static void launch_dec(const DecArgs& a, size_t shbytes, hipStream_t s) {
-  if (a.k <= 8)
-    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, 8, 1>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
-  else
-    hipLaunchKernelGGL((k_decode_layer<KCG, KCD, kDecMaxK, 1>), dim3(kDecBlocks), dim3(kDecThreads), shbytes, s, a);
+static const void* dec_kernel(int k) {
+  return k <= 8 ? reinterpret_cast<const void*>(&k_decode_layer<KCG, KCD, 8, 1>)
+                : reinterpret_cast<const void*>(&k_decode_layer<KCG, KCD, kDecMaxK, 1>);
+}
+
+// The kernel instantiation and dynamic LDS bytes of the fused layer for (d, T),
+// where decode_supported(d, T).
+static const void* dec_plan(const moe_dims& d, int T, size_t* shbytes) {
+  const size_t ldh = static_cast<size_t>(div_up(max(d.inter, d.shared_inter), 8) * 8);
+  *shbytes = static_cast<size_t>(T) * (d.top_k + 1) * ldh * 2;   // h of all slots in LDS
+  if (T > 1)   // decode_supported(): hidden <= 2048, inter and shared_inter <= 512, k <= 8
+    return reinterpret_cast<const void*>(&k_decode_layer<1, 1, 8, kDecMaxT>);
+  const int kcg = static_cast<int>(div_up(d.hidden, 2048));
+  const int kcd = static_cast<int>(div_up(max(d.inter, d.shared_inter), 512));
+  switch (kcg * 10 + kcd) {   // decode_supported(): both 1 or 2
+    case 11: return dec_kernel<1, 1>(d.top_k);
+    case 12: return dec_kernel<1, 2>(d.top_k);
+    case 21: return dec_kernel<2, 1>(d.top_k);
+    default: return dec_kernel<2, 2>(d.top_k);
+  }
+}
+
+hipError_t decode_residency(const moe_dims& d, int T, int* needed, int* resident) {
+  *needed = kDecBlocks;
+  *resident = 0;
+  size_t sh = 0;
+  const void* kern = dec_plan(d, T, &sh);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kDecThreads, sh);
+  if (e != hipSuccess) return e;
+  *resident = cus * per_cu;
+  return hipSuccess;
 }
 
 hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, int T, uint16_t* y,
@@ -540,20 +573,11 @@ hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint
   a.ldh = static_cast<int>(div_up(max(d.inter, d.shared_inter), 8) * 8);
   a.y = y;
   a.sync = reinterpret_cast<DecSync*>(p.sync);
-  const size_t sh = static_cast<size_t>(T) * (d.top_k + 1) * a.ldh * 2;   // h of all slots in LDS
-  if (T > 1) {   // decode_supported(): hidden <= 2048, inter and shared_inter <= 512, k <= 8
-    hipLaunchKernelGGL((k_decode_layer<1, 1, 8, kDecMaxT>), dim3(kDecBlocks), dim3(kDecThreads), sh, s, a);
-    return hipGetLastError();
-  }
-  const int kcg = static_cast<int>(div_up(d.hidden, 2048));
-  const int kcd = static_cast<int>(div_up(max(d.inter, d.shared_inter), 512));
-  switch (kcg * 10 + kcd) {   // decode_supported(): both 1 or 2
-    case 11: launch_dec<1, 1>(a, sh, s); break;
-    case 12: launch_dec<1, 2>(a, sh, s); break;
-    case 21: launch_dec<2, 1>(a, sh, s); break;
-    default: launch_dec<2, 2>(a, sh, s); break;
-  }
-  return hipGetLastError();
+  a.err = p.err;
+  size_t sh = 0;
+  const void* kern = dec_plan(d, T, &sh);
+  void* args[] = {&a};
+  return hipLaunchKernel(kern, dim3(kDecBlocks), dim3(kDecThreads), args, sh, s);
 }
 
 }  // namespace moe

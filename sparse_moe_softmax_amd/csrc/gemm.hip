@@ -40,11 +40,14 @@
 //   SWIGLU : wave columns = 32 gate rows + the matching 32 up rows;
 //            h = bf16( silu(gate) * up ) in grouped order.
 //   SCATTER: y[token][col] += weight * o, fp32 atomics (standalone op).
-//   SLOTS  : slot[token][j][col] = fp16(weight * o): the output of slot j of
-//            the token (routed: times its routing weight; shared expert: slot
-//            k, times the sigmoid gate) or, without weights, fp16(o) for the
-//            combine to weight; token-major, for a fixed-order combine
-//            afterwards.  No atomics.
+//   SLOTS  : the unweighted output o of slot j of a token (routed slots
+//            j < k, the shared expert's slot k), token-major [T][k+1][H], as
+//            fp16 with a power-of-two exponent per (slot row, 64 columns):
+//            slot = fp16(o * 2^-e), e >= 0 the smallest that keeps the
+//            64-value chunk below 2^15, so the range is fp32's and every value
+//            keeps fp16's 11-bit precision unless it lies 2^24 below its
+//            chunk's largest.  The combine weights and sums them afterwards in
+//            a fixed order.  No atomics.
 //
 // Launch order is XCD-aware: consecutive workgroup ids go round-robin to the 8
 // XCDs, so ids are mapped such that all column slices of one tile share an XCD
@@ -74,6 +77,25 @@ static_assert(kRingBytes % 256 == 0, "ring alignment");
 
 enum { kSwiglu = 0, kScatter = 1, kSlots = 2 };
 
+// Slot epilogue staging: a wave's 32 x 64 fp32 sub-tile, rows padded to 72 floats.
+constexpr int kSlotRowFloats = 72;
+constexpr int kSlotStageBytes = 32 * kSlotRowFloats * 4;
+static_assert(4 * kSlotStageBytes <= kRingBytes, "slot staging fits the ring");
+
+// Exponent e >= 0 of a slot chunk whose largest magnitude is mx: the smallest
+// with mx * 2^-e < 2^15, so that fp16 rounding of every scaled value stays
+// finite (fp16's largest finite value is 65504).  Integer work on the bits:
+// floor(log2(mx)) = biased exponent - 127 for normal mx; 0 for mx < 2^15.
+__device__ inline int slot_exponent(float mx) {
+  const int fl = static_cast<int>((__float_as_uint(mx) >> 23) & 255u) - 127;
+  return max(0, fl - 14);
+}
+// Two floats -> two fp16 (round to nearest even), low half first.
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2 h = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 struct GemmArgs {
   // index 0: routed experts, 1: shared expert
   const uint8_t* packed[2];   // matrix-core layout
@@ -90,8 +112,10 @@ struct GemmArgs {
   const int32_t* block_map;
   const int32_t* n_tiles;
   const int32_t* tile_rows;   // rows per routed tile (NULL: from offsets)
-  const float* row_w;   // routed: weight per flat slot
-  const float* gate;    // shared: sigmoid gate per token
+  const float* row_w;   // routed: weight per flat slot (SCATTER)
+  const float* gate;    // shared: sigmoid gate per token (SCATTER)
+  uint8_t* slot_exp;    // SLOTS: exponent e per (slot row, 64 columns), [T][k+1][H/64]
+  int gather;           // routed A rows: 1 = token rows a[perm[p] / k], 0 = a[p]
   int block_m;
   int n_sh;             // shared chunks (first in the chunk order)
   int max_tiles;
@@ -146,7 +170,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
     const int r = (wave * kAI + j) * 8 + (lane >> 3);   // tile row this lane fills
     arow_idx[j] = t.row0 + min(r, t.rows - 1);         // padding rows re-read the last live row
   }
-  if (MODE == kSwiglu && t.which == 0) {
+  if (g.gather && t.which == 0) {
     int pr[kAI];
 #pragma unroll
     for (int j = 0; j < kAI; ++j) pr[j] = g.perm[arow_idx[j]];
@@ -320,8 +344,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s)
     if (s < kg) issue(s);
-  // unweighted slots: this thread's row's flat slot, needed only at the epilogue
-  const bool deferred_rows = MODE == kSlots && g.row_w == nullptr;
+  // slots: this thread's row's flat slot, needed only at the epilogue
+  constexpr bool deferred_rows = MODE == kSlots;
   int my_f = 0;
   if (deferred_rows && t.which == 0 && static_cast<int>(threadIdx.x) < t.rows) my_f = g.perm[t.row0 + threadIdx.x];
   const int steady_end = kg - (kStages - 1);   // iterations kb < steady_end are steady
@@ -366,7 +390,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
       const int k = g.k;
       s_drow[r] = t.which == 1 ? static_cast<int64_t>(t.row0 + r) * (k + 1) + k
                                : static_cast<int64_t>(my_f / k) * (k + 1) + (my_f % k);
-      s_wt[r] = 1.0f;
     }
     __syncthreads();
   }
@@ -399,25 +422,47 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
       __builtin_amdgcn_wave_barrier();
     }
   } else if (MODE == kSlots) {
+    // Each wave stages a 32-row sub-tile of its 64 columns as fp32 (rows of 72
+    // floats: the two lane halves of a store hit disjoint banks), then 8 lanes
+    // per row take the row's largest magnitude, pick the exponent e and store
+    // fp16(o * 2^-e) as 16 contiguous bytes per lane, lane 0 of the 8 the
+    // exponent byte.
     uint16_t* out = static_cast<uint16_t*>(g.out[0]);   // [T][k+1][H] fp16
     const int H = g.H;
+    const int n_chunks = H >> 6;
+    float* stf = reinterpret_cast<float*>(ring + wave * kSlotStageBytes);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      // 32 rows x 64 columns, fp16 (128 B per row)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = (j >> 2) * 8 + gq * 4 + (j & 3);
-        const float wt = s_wt[m * 32 + r];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          reinterpret_cast<_Float16*>(stg)[r * 64 + c * 32 + col] = static_cast<_Float16>(wt * acc[m][c][j]);
+        for (int c = 0; c < 2; ++c) stf[r * kSlotRowFloats + c * 32 + col] = acc[m][c][j];
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
         const int r = part * 8 + (lane >> 3), pc = lane & 7;
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * 128 + pc * 16);
-        if (m * 32 + r < rows) *reinterpret_cast<uint4*>(out + s_drow[m * 32 + r] * H + t.n0 + pc * 8) = v;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(stf + r * kSlotRowFloats + pc * 8);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(stf + r * kSlotRowFloats + pc * 8 + 4);
+        float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                         fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+        // largest over the row's 8 lanes: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0xB1, 0xF, 0xF, false)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x4E, 0xF, 0xF, false)));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x141, 0xF, 0xF, false)));
+        const int e = slot_exponent(mx);
+        const float sc = __int_as_float((127 - e) << 23);   // 2^-e, exact scaling
+        uint4 o;
+        o.x = pack_f16x2(v0.x * sc, v0.y * sc);
+        o.y = pack_f16x2(v0.z * sc, v0.w * sc);
+        o.z = pack_f16x2(v1.x * sc, v1.y * sc);
+        o.w = pack_f16x2(v1.z * sc, v1.w * sc);
+        if (m * 32 + r < rows) {
+          const int64_t drow = s_drow[m * 32 + r];
+          *reinterpret_cast<uint4*>(out + drow * H + t.n0 + pc * 8) = o;
+          if (pc == 0) g.slot_exp[drow * n_chunks + (t.n0 >> 6)] = static_cast<uint8_t>(e);
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -489,23 +534,23 @@ __global__ __launch_bounds__(kGemmThreads, kGemmOcc) void k_gemm_q4(GemmArgs g) 
   t.pbase = g.packed[t.which] + static_cast<int64_t>(e) * g.expert_bytes[t.which] +
             static_cast<int64_t>(slice) * t.kg * kPackBlock;
 
-  // Output row and weight of every tile row (down projection epilogues).  With
-  // row weights (scatter, weighted slots) they are filled before the K loop,
-  // whose first barrier publishes them.  Unweighted slots need only the output
-  // row: gemm_tile loads the permutation after issuing its first stages and
-  // fills s_drow at the epilogue, so that load adds no latency to the start.
+  // Output row and weight of every tile row (down projection epilogues).  The
+  // scatter epilogue fills them before the K loop, whose first barrier
+  // publishes them.  Slots need only the output row: gemm_tile loads the
+  // permutation after issuing its first stages and fills s_drow at the
+  // epilogue, so that load adds no latency to the start.
   __shared__ int64_t s_drow[kBM];
   __shared__ float s_wt[kBM];
-  if (MODE != kSwiglu && !(MODE == kSlots && g.row_w == nullptr)) {
+  if (MODE == kScatter) {
     for (int r = tid; r < t.rows; r += kGemmThreads) {
       const int k = g.k;
       if (t.which == 1) {
         const int tok = t.row0 + r;
-        s_drow[r] = (MODE == kSlots) ? static_cast<int64_t>(tok) * (k + 1) + k : tok;
-        s_wt[r] = g.gate ? g.gate[tok] : 1.0f;   // without a gate the combine applies it
+        s_drow[r] = tok;
+        s_wt[r] = g.gate ? g.gate[tok] : 1.0f;
       } else {
         const int f = g.perm[t.row0 + r];
-        s_drow[r] = (MODE == kSlots) ? static_cast<int64_t>(f / k) * (k + 1) + (f % k) : f / k;
+        s_drow[r] = f / k;
         s_wt[r] = g.row_w[f];
       }
     }
@@ -555,7 +600,7 @@ static void fill_common(GemmArgs& g, const moe_dims& d, const GemmTiles& tl, int
 }
 
 hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* x,
-                              const GemmTiles& tl, int T, uint16_t* h, uint16_t* h_sh, hipStream_t s) {
+                              bool gather, const GemmTiles& tl, int T, uint16_t* h, uint16_t* h_sh, hipStream_t s) {
   GemmArgs g{};
   g.packed[0] = w.packed;
   g.expert_bytes[0] = pack_geom(d, MOE_MAT_GATE_UP).expert_bytes;
@@ -578,6 +623,7 @@ hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* 
     g.ldo[1] = d.shared_inter;
   }
   fill_common(g, d, tl, T, w_sh != nullptr);
+  g.gather = gather ? 1 : 0;
   const int wmax = w_sh ? max(d.inter, d.shared_inter) : d.inter;
   g.n_slices = static_cast<int>(div_up(wmax, 128));
   const int grid = gemm_grid(g.n_sh + g.max_tiles, g.n_slices);
@@ -585,7 +631,7 @@ hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* 
   return hipGetLastError();
 }
 
-static GemmArgs down_args(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
+static GemmArgs down_args(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h, bool gather,
                           const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate, int T,
                           void* out) {
   GemmArgs g{};
@@ -608,6 +654,7 @@ static GemmArgs down_args(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh
     g.ldo[1] = d.hidden;
   }
   fill_common(g, d, tl, T, w_sh != nullptr);
+  g.gather = gather ? 1 : 0;
   g.row_w = row_w;
   g.gate = gate;
   g.n_slices = static_cast<int>(div_up(d.hidden, 256));
@@ -615,18 +662,19 @@ static GemmArgs down_args(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh
 }
 
 hipError_t launch_gemm_scatter(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
-                               const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate,
-                               int T, float* y, hipStream_t s) {
-  GemmArgs g = down_args(d, w, w_sh, h, h_sh, tl, row_w, gate, T, y);
+                               bool gather, const uint16_t* h_sh, const GemmTiles& tl, const float* row_w,
+                               const float* gate, int T, float* y, hipStream_t s) {
+  GemmArgs g = down_args(d, w, w_sh, h, gather, h_sh, tl, row_w, gate, T, y);
   const int grid = gemm_grid(g.n_sh + g.max_tiles, g.n_slices);
   hipLaunchKernelGGL(k_gemm_q4<kScatter>, dim3(grid), dim3(kGemmThreads), 0, s, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_slots(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
-                             const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate, int T,
-                             uint16_t* slots, hipStream_t s) {
-  GemmArgs g = down_args(d, w, w_sh, h, h_sh, tl, row_w, gate, T, slots);
+                             const uint16_t* h_sh, const GemmTiles& tl, int T, uint16_t* slots, uint8_t* slot_exp,
+                             hipStream_t s) {
+  GemmArgs g = down_args(d, w, w_sh, h, false, h_sh, tl, nullptr, nullptr, T, slots);
+  g.slot_exp = slot_exp;
   const int grid = gemm_grid(g.n_sh + g.max_tiles, g.n_slices);
   hipLaunchKernelGGL(k_gemm_q4<kSlots>, dim3(grid), dim3(kGemmThreads), 0, s, g);
   return hipGetLastError();
@@ -678,14 +726,17 @@ hipError_t launch_prepack_q4(const moe_dims& d, int matrix, const moe_q4& w, int
   return hipGetLastError();
 }
 
-// out[t][n] = bf16( sum_{j<k} w[t][j] * slot[t][j][n] + gate[t] * slot[t][k][n] ),
-// slots fp16, summed in fp32 in slot order (shared expert last); w or gate
-// NULL = weights of 1 (slots already weighted).  8 columns per thread.  With
-// k known at compile time (K > 0) all k + 1 slot vectors are requested before
-// the sum, so a thread waits for one memory round trip, not k + 1; K = 0 takes
-// k at run time.
+// out[t][n] = bf16( sum_{j<k} w[t][j] * o_j + gate[t] * o_k ), o_j = slot[t][j][n] * 2^e[t][j][n/64]
+// (fp16 slot values and their chunk exponents as the slot epilogue wrote
+// them), summed in fp32 in slot order (shared expert last); w or gate NULL =
+// weights of 1.  The weight and 2^e are multiplied first (exact: a power-of-two
+// scaling), so each term is the single rounding of w * o.  8 columns per
+// thread.  With k known at compile time (K > 0) all k + 1 slot vectors and
+// exponents are requested before the sum, so a thread waits for one memory
+// round trip, not k + 1; K = 0 takes k at run time.
 template <int K>
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ slots, const float* __restrict__ w,
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ slots,
+                                                 const uint8_t* __restrict__ slot_exp, const float* __restrict__ w,
                                                  const float* __restrict__ gate, uint16_t* __restrict__ out, int T,
                                                  int H, int k_rt) {
   const int k = K > 0 ? K : k_rt;
@@ -694,31 +745,38 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
   if (i >= static_cast<int64_t>(T) * per_tok) return;
   const int64_t t = i / per_tok;
   const int c8 = static_cast<int>(i % per_tok) * 8;
+  const int n_chunks = H >> 6;
   const uint16_t* src = slots + t * (k + 1) * H + c8;
+  const uint8_t* esrc = slot_exp + t * (k + 1) * n_chunks + (c8 >> 6);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add = [&](const uint4& v, float wj) {
+  auto add = [&](const uint4& v, float wj, uint32_t e) {
+    const float we = wj * __uint_as_float((127u + e) << 23);   // w * 2^e
     const f16x2 p[4] = {__builtin_bit_cast(f16x2, v.x), __builtin_bit_cast(f16x2, v.y),
                         __builtin_bit_cast(f16x2, v.z), __builtin_bit_cast(f16x2, v.w)};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      acc[2 * u] = __builtin_fmaf(wj, static_cast<float>(p[u].x), acc[2 * u]);
-      acc[2 * u + 1] = __builtin_fmaf(wj, static_cast<float>(p[u].y), acc[2 * u + 1]);
+      acc[2 * u] = __builtin_fmaf(we, static_cast<float>(p[u].x), acc[2 * u]);
+      acc[2 * u + 1] = __builtin_fmaf(we, static_cast<float>(p[u].y), acc[2 * u + 1]);
     }
   };
   if constexpr (K > 0) {
     uint4 v[K + 1];
+    uint32_t e[K + 1];
 #pragma unroll
-    for (int j = 0; j <= K; ++j) v[j] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
+    for (int j = 0; j <= K; ++j) {
+      v[j] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
+      e[j] = esrc[j * n_chunks];
+    }
     float wj[K + 1];
 #pragma unroll
     for (int j = 0; j < K; ++j) wj[j] = w ? w[t * K + j] : 1.0f;
     wj[K] = gate ? gate[t] : 1.0f;
 #pragma unroll
-    for (int j = 0; j <= K; ++j) add(v[j], wj[j]);
+    for (int j = 0; j <= K; ++j) add(v[j], wj[j], e[j]);
   } else {
     for (int j = 0; j <= k; ++j) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
-      add(v, j == k ? (gate ? gate[t] : 1.0f) : (w ? w[t * k + j] : 1.0f));
+      add(v, j == k ? (gate ? gate[t] : 1.0f) : (w ? w[t * k + j] : 1.0f), esrc[j * n_chunks]);
     }
   }
   uint4 o;
@@ -729,14 +787,14 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
   *reinterpret_cast<uint4*>(out + t * H + c8) = o;
 }
 
-hipError_t launch_combine(const uint16_t* slots, const float* w, const float* gate, uint16_t* out, int T, int H, int k,
-                          hipStream_t s) {
+hipError_t launch_combine(const uint16_t* slots, const uint8_t* slot_exp, const float* w, const float* gate,
+                          uint16_t* out, int T, int H, int k, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(T) * (H / 8);
   const dim3 grid(static_cast<unsigned>(div_up(n, 256)));
   if (k == 8)
-    hipLaunchKernelGGL(k_combine<8>, grid, dim3(256), 0, s, slots, w, gate, out, T, H, k);
+    hipLaunchKernelGGL(k_combine<8>, grid, dim3(256), 0, s, slots, slot_exp, w, gate, out, T, H, k);
   else
-    hipLaunchKernelGGL(k_combine<0>, grid, dim3(256), 0, s, slots, w, gate, out, T, H, k);
+    hipLaunchKernelGGL(k_combine<0>, grid, dim3(256), 0, s, slots, slot_exp, w, gate, out, T, H, k);
   return hipGetLastError();
 }
 

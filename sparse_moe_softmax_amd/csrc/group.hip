@@ -9,26 +9,42 @@
 //   2. per expert: exclusive scan of its count over the tiles  (k_group_scan, one block per expert)
 //   3. per tile: stable in-tile ranks from wavefront ballots,
 //      positions = offsets[e] + tile base + rank               (k_group_scatter)
-// Integer counting only, so every output is bitwise deterministic.
+// Integer counting only, so every output is bitwise deterministic.  An id
+// outside [0, E) (possible only for caller-supplied ids) is skipped: it is not
+// counted, its slot gets no position (inv_perm -1), and the MOE_DEVERR_EXPERT_ID
+// bit is set in the error word when one is given.
 #include "internal.hpp"
 
 namespace moe {
 
+__device__ inline void flag_bad_id(uint32_t* err) {
+  if (err)
+    __hip_atomic_fetch_or(err, static_cast<uint32_t>(MOE_DEVERR_EXPERT_ID), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(256) void k_tile_hist(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                   int32_t* __restrict__ tilehist) {
+                                                   int32_t* __restrict__ tilehist, uint32_t* __restrict__ err) {
   __shared__ int hist[256];
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
   const int64_t f0 = static_cast<int64_t>(blockIdx.x) * kTopkTile * k;
   const int64_t f1 = min(static_cast<int64_t>(T) * k, f0 + static_cast<int64_t>(kTopkTile) * k);
-  for (int64_t f = f0 + threadIdx.x; f < f1; f += 256) atomicAdd(&hist[ids[f]], 1);
+  for (int64_t f = f0 + threadIdx.x; f < f1; f += 256) {
+    const int e = ids[f];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E))
+      atomicAdd(&hist[e], 1);
+    else
+      flag_bad_id(err);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) tilehist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
 }
 
-hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, hipStream_t s) {
+hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, uint32_t* err,
+                            hipStream_t s) {
   hipLaunchKernelGGL(k_tile_hist, dim3(static_cast<unsigned>(div_up(T, kTopkTile))), dim3(256), 0, s, ids, T, k, E,
-                     tilehist);
+                     tilehist, err);
   return hipGetLastError();
 }
 
@@ -84,7 +100,7 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
                                                        int32_t* __restrict__ block_map, int max_tiles,
                                                        int32_t* __restrict__ n_tiles, int write_map,
-                                                       int32_t* __restrict__ tile_rows) {
+                                                       int32_t* __restrict__ tile_rows, uint32_t* __restrict__ err) {
   __shared__ int base[256];
   __shared__ int sm[4];
   const int tid = threadIdx.x;
@@ -128,8 +144,14 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
     const int64_t f1 = min(static_cast<int64_t>(T) * k, f0 + static_cast<int64_t>(kTopkTile) * k);
     for (int64_t fb = f0; fb < f1; fb += 64) {
       const int64_t f = fb + lane;
-      const bool valid = f < f1;
-      const int e = valid ? ids[f] : 0;
+      const bool in_tile = f < f1;
+      const int id = in_tile ? ids[f] : 0;
+      const bool valid = in_tile && static_cast<unsigned>(id) < static_cast<unsigned>(E);
+      if (in_tile && !valid) {
+        inv_perm[f] = -1;
+        flag_bad_id(err);
+      }
+      const int e = valid ? id : 0;
       uint64_t match = __ballot(valid);
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
@@ -159,20 +181,21 @@ hipError_t launch_group_counts(const int32_t* tilehist, int32_t* tilebase, int T
 hipError_t launch_group_scatter(const int32_t* ids, const int32_t* counts, const int32_t* tilebase, int T, int k,
                                 int E, int block_m, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                                 int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map,
-                                int32_t* tile_rows, hipStream_t s) {
+                                int32_t* tile_rows, uint32_t* err, hipStream_t s) {
   const int ntile = static_cast<int>(div_up(T, kTopkTile));
   hipLaunchKernelGGL(k_group_scatter, dim3(ntile), dim3(256), 0, s, ids, counts, tilebase, T, k, E, block_m, offsets,
-                     perm, inv_perm, block_map, max_tiles, n_tiles, write_map ? 1 : 0, tile_rows);
+                     perm, inv_perm, block_map, max_tiles, n_tiles, write_map ? 1 : 0, tile_rows, err);
   return hipGetLastError();
 }
 
 hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
                         int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                        int32_t* block_map, int max_tiles, int32_t* n_tiles, int32_t* tile_rows, hipStream_t s) {
-  hipError_t err = launch_group_counts(tilehist, tilebase, T, E, counts, s);
-  if (err != hipSuccess) return err;
+                        int32_t* block_map, int max_tiles, int32_t* n_tiles, int32_t* tile_rows, uint32_t* err,
+                        hipStream_t s) {
+  const hipError_t e = launch_group_counts(tilehist, tilebase, T, E, counts, s);
+  if (e != hipSuccess) return e;
   return launch_group_scatter(ids, counts, tilebase, T, k, E, block_m, offsets, perm, inv_perm, block_map, max_tiles,
-                              n_tiles, true, tile_rows, s);
+                              n_tiles, true, tile_rows, err, s);
 }
 
 }  // namespace moe

@@ -303,7 +303,8 @@ hipError_t launch_router_gemv(const uint16_t* x, const float* w, const float* bi
 hipError_t launch_topk(const float* parts, const float* s_parts, int splits, const float* bias, int T, int E, int k,
                        float* logits_out, float* s_out, int32_t* ids, float* wts, float* gate, int32_t* tilehist,
                        hipStream_t s);
-hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, hipStream_t s);
+// err (nullable): device error word; ids outside [0, E) set MOE_DEVERR_EXPERT_ID and are skipped.
+hipError_t launch_tile_hist(const int32_t* ids, int T, int k, int E, int32_t* tilehist, uint32_t* err, hipStream_t s);
 // The two halves of launch_group: per-expert counts (and per-tile bases), then
 // offsets + permutation (+ block map and n_tiles when write_map).
 hipError_t launch_group_counts(const int32_t* tilehist, int32_t* tilebase, int T, int E, int32_t* counts,
@@ -312,23 +313,27 @@ hipError_t launch_group_counts(const int32_t* tilehist, int32_t* tilebase, int T
 hipError_t launch_group_scatter(const int32_t* ids, const int32_t* counts, const int32_t* tilebase, int T, int k,
                                 int E, int block_m, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                                 int32_t* block_map, int max_tiles, int32_t* n_tiles, bool write_map,
-                                int32_t* tile_rows, hipStream_t s);
+                                int32_t* tile_rows, uint32_t* err, hipStream_t s);
 hipError_t launch_group(const int32_t* ids, const int32_t* tilehist, int32_t* tilebase, int T, int k, int E,
                         int block_m, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
-                        int32_t* block_map, int max_tiles, int32_t* n_tiles, int32_t* tile_rows, hipStream_t s);
+                        int32_t* block_map, int max_tiles, int32_t* n_tiles, int32_t* tile_rows, uint32_t* err,
+                        hipStream_t s);
+// gather: routed A rows are token rows a[perm[p] / k] (else grouped rows a[p]).
 hipError_t launch_gemm_swiglu(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* x,
-                              const GemmTiles& tl, int T, uint16_t* h, uint16_t* h_sh, hipStream_t s);
+                              bool gather, const GemmTiles& tl, int T, uint16_t* h, uint16_t* h_sh, hipStream_t s);
 hipError_t launch_gemm_scatter(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
-                               const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate,
-                               int T, float* y, hipStream_t s);
-// Down GEMM writing fp16 weighted slot outputs slot[t][j][:] (routed j < k, shared j = k).
+                               bool gather, const uint16_t* h_sh, const GemmTiles& tl, const float* row_w,
+                               const float* gate, int T, float* y, hipStream_t s);
+// Down GEMM writing every slot's unweighted output, slot[t][j][:] (routed j < k,
+// shared j = k), as fp16 with a power-of-two exponent per 64 columns in
+// slot_exp [T][k+1][H/64].
 hipError_t launch_gemm_slots(const moe_dims& d, const moe_q4& w, const moe_q4* w_sh, const uint16_t* h,
-                             const uint16_t* h_sh, const GemmTiles& tl, const float* row_w, const float* gate, int T,
-                             uint16_t* slots, hipStream_t s);
-// out[t] = bf16( sum_{j<k} w[t][j] * slot[t][j] + gate[t] * slot[t][k] ) in slot order
-// (w or gate NULL = 1).
-hipError_t launch_combine(const uint16_t* slots, const float* w, const float* gate, uint16_t* out, int T, int H, int k,
-                          hipStream_t s);
+                             const uint16_t* h_sh, const GemmTiles& tl, int T, uint16_t* slots, uint8_t* slot_exp,
+                             hipStream_t s);
+// out[t] = bf16( sum_{j<k} w[t][j] * o_j + gate[t] * o_k ) in slot order, o_j the
+// slot values times 2^exponent (w or gate NULL = 1).
+hipError_t launch_combine(const uint16_t* slots, const uint8_t* slot_exp, const float* w, const float* gate,
+                          uint16_t* out, int T, int H, int k, hipStream_t s);
 struct DecodePtrs {
   float* logits;
   float* s_logit;
@@ -336,6 +341,7 @@ struct DecodePtrs {
   float* wts;
   float* gate;
   void* sync;        // decode_sync_bytes(), zero before the first call on it
+  uint32_t* err;     // device error word (MOE_DEVERR_* bits)
 };
 // The whole layer for 1 <= T <= kDecMaxT tokens as one launch (router, top-k,
 // experts, combine), where decode_supported(d, T).
@@ -343,6 +349,9 @@ constexpr int kDecMaxT = 4;
 hipError_t launch_decode_layer(const moe_dims& d, const moe_layer& L, const uint16_t* x, int T, uint16_t* y,
                                const DecodePtrs& p, hipStream_t s);
 bool decode_supported(const moe_dims& d, int T);
+// Workgroups the fused layer for (d, T) launches, and how many of its
+// workgroups the current device holds at once.
+hipError_t decode_residency(const moe_dims& d, int T, int* needed, int* resident);
 size_t decode_sync_bytes(const moe_dims& d);
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }

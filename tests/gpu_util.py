@@ -65,26 +65,40 @@ def assert_layer_close(gpu_bits, ref_bits, what=""):
     return max_rel, l1_rel
 
 
-def forward_and_check(d, lay: synth.Layer, x_cpu: torch.Tensor, tokens=None, threads: int = 0, dl=None):
+def forward_and_check(d, lay: synth.Layer, x_cpu: torch.Tensor, tokens=None, threads: int = 0, dl=None,
+                      host_routing: bool = False, logit_atol: float = LOGIT_ATOL):
     """Run moe_forward on the GPU and check it against the oracle with the
-    shared-logits protocol: logits within LOGIT_ATOL; the oracle's top-k of
+    shared-logits protocol: logits within logit_atol; the oracle's top-k of
     the GPU logits equals the GPU ids bit for bit and its weights are within
     WEIGHT_ATOL; the oracle layer output from those ids meets the parity bar
-    on ``tokens`` (all tokens if None)."""
+    on ``tokens`` (all tokens if None).
+
+    host_routing: run moe_forward_host_routing instead (grouped path only).
+    It has no logits output; its router and top-k are moe_forward's stages, so
+    the logits come from those stages run alone on a second workspace."""
     m = moe()
     dl = dl or device_layer(lay, d)
     T = x_cpu.shape[0]
     x = x_cpu.to("cuda")
+    md = to_dims(d)
     logits = torch.empty((T, d.n_experts), dtype=torch.float32, device="cuda")
     ids = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, d.top_k), dtype=torch.float32, device="cuda")
-    y = m.moe_forward(to_dims(d), dl, x, logits_out=logits, ids_out=ids, w_out=wts)
+    ws = m.moe_workspace(md, T)
+    if host_routing:
+        y = m.moe_forward_host_routing(md, dl, x, ids_out=ids, w_out=wts, workspace=ws)
+        ws2 = m.moe_workspace(md, T)
+        scratch = torch.empty((T, d.hidden), dtype=torch.bfloat16, device="cuda")
+        m.moe_forward_stages(md, dl, x, scratch, ws2, 0, 1, logits_out=logits)
+    else:
+        y = m.moe_forward(md, dl, x, logits_out=logits, ids_out=ids, w_out=wts, workspace=ws)
     torch.cuda.synchronize()
+    assert m.moe_workspace_errors(ws) == 0
     ow = oracle_layer(lay)
     xb = synth.bf16_bits_numpy(x_cpu)
     o_logits, o_s = oracle.router(xb, ow.router_w, ow.router_bias, ow.shared_gate_w, threads)
     g_logits = logits.cpu().numpy()
-    assert np.abs(g_logits - o_logits).max() <= LOGIT_ATOL
+    assert np.abs(g_logits - o_logits).max() <= logit_atol
     o_ids, o_w = oracle.topk(g_logits, d.top_k)
     g_ids = ids.cpu().numpy()
     assert np.array_equal(g_ids, o_ids)
@@ -94,4 +108,4 @@ def forward_and_check(d, lay: synth.Layer, x_cpu: torch.Tensor, tokens=None, thr
     o_out, _, _, _ = oracle.moe_tokens(odims(d), xb, o_ids, o_w, o_g, ow, tokens=tok, threads=threads)
     g_out = bits(y)[tok]
     errs = assert_layer_close(g_out, o_out, f"T={T}")
-    return {"y": y, "ids": g_ids, "logits": g_logits, "errs": errs}
+    return {"y": y, "ids": g_ids, "logits": g_logits, "errs": errs, "ref_bits": o_out}

@@ -81,12 +81,50 @@ def test_bad_arguments_rejected(m):
     assert L.moe_group(*args(64, mt, need - 1)) == -3
     # grouped gemm: block_m above the kernel tile, scatter without weights, unknown epilogue
     q = m._Q4(FAKE, FAKE, FAKE, FAKE)
-    g = lambda epi, bm, rw: L.moe_grouped_gemm_q4(d, ctypes.byref(q), epi, FAKE, FAKE, FAKE, FAKE, FAKE, 10, rw,
-                                                  100, bm, FAKE, None)
+    g = lambda epi, bm, rw, tok=1: L.moe_grouped_gemm_q4(d, ctypes.byref(q), epi, FAKE, tok, FAKE, FAKE, FAKE, FAKE,
+                                                         10, rw, 100, bm, FAKE, None)
     assert g(0, m.moe_block_m() + 1, None) == -1
     assert g(1, 64, None) == -1
     assert g(7, 64, FAKE) == -1
     assert "epilogue" in L.moe_last_error_message().decode()
+    assert g(0, 64, None, tok=2) == -1
+    assert "a_rows_are_tokens" in L.moe_last_error_message().decode()
+    assert L.moe_grouped_gemm_q4(d, ctypes.byref(m._Q4(FAKE, FAKE, FAKE, None)), 0, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                                 10, None, 100, 64, FAKE, None) == -1           # not prepacked
+    assert "moe_prepack_q4" in L.moe_last_error_message().decode()
+
+
+def test_workspace_header_and_error_query(m):
+    """Both workspaces start with the 256-byte header that holds the device
+    error word; the query refuses a missing or short workspace and a NULL
+    output before touching the device."""
+    L = m.lib()
+    d = _d(m)
+    assert m.WORKSPACE_HEADER_BYTES == 256
+    ntile = -(-100 // 16)
+    assert L.moe_group_workspace_bytes(d, 100) == 256 + 2 * (-(-ntile * 256 * 4 // 256) * 256)
+    flags = ctypes.c_int32(7)
+    assert L.moe_workspace_errors(None, 1 << 20, 0, ctypes.byref(flags), None) == -3
+    assert L.moe_workspace_errors(FAKE, 255, 0, ctypes.byref(flags), None) == -3
+    assert L.moe_workspace_errors(FAKE, 256, 0, None, None) == -1
+    assert flags.value == 7
+    assert (m.MOE_DEVERR_HANDOVER_TIMEOUT, m.MOE_DEVERR_EXPERT_ID) == (1, 2)
+
+
+def test_fused_residency_checks(m):
+    """The residency query: only the fused sizes, outputs required; without a
+    device it reports a HIP error instead of guessing (the forward path then
+    refuses to launch the fused layer)."""
+    L = m.lib()
+    n, r = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    assert L.moe_fused_residency(_d(m), 5, ctypes.byref(n), ctypes.byref(r)) == -2      # grouped path
+    assert L.moe_fused_residency(_d(m, hidden=4096), 2, ctypes.byref(n), ctypes.byref(r)) == -2
+    assert L.moe_fused_residency(_d(m), 1, None, ctypes.byref(r)) == -1
+    assert L.moe_fused_residency(_d(m, group_size=32), 1, ctypes.byref(n), ctypes.byref(r)) == -2
+    import torch
+    if not torch.cuda.is_available():
+        assert L.moe_fused_residency(_d(m), 1, ctypes.byref(n), ctypes.byref(r)) == -4
+        assert (n.value, r.value) == (0, 0)
 
 
 def test_forward_workspace_checked(m):

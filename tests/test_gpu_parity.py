@@ -220,21 +220,28 @@ def _h_compare(h_gpu_bits, h_ref_bits):
     assert np.all(np.abs(g - r) <= allowed)
 
 
-@pytest.mark.parametrize("dname,T,mode,bm", [("tiny", 24, "uniform", 128), ("tiny", 300, "one_hot", 128),
-                                             ("model", 64, "uniform", 128), ("model", 700, "zipf", 128),
-                                             ("model", 200, "uniform", 37)])
-def test_grouped_gemm_swiglu(dname, T, mode, bm):
-    say("grouped gemm swiglu", dname, T, mode, bm)
+@pytest.mark.parametrize("dname,T,mode,bm,tokens", [("tiny", 24, "uniform", 128, True),
+                                                    ("tiny", 300, "one_hot", 128, True),
+                                                    ("model", 64, "uniform", 128, True),
+                                                    ("model", 700, "zipf", 128, True),
+                                                    ("model", 200, "uniform", 37, True),
+                                                    ("model", 200, "uniform", 37, False),
+                                                    ("tiny", 300, "zipf", 128, False)])
+def test_grouped_gemm_swiglu(dname, T, mode, bm, tokens):
+    """a_rows_are_tokens = 1: token rows of x gathered through perm; 0: the
+    same rows handed over already in grouped order (a[p] = x[perm[p] / k])."""
+    say("grouped gemm swiglu", dname, T, mode, bm, tokens)
     m = gu.moe()
     d = TINY if dname == "tiny" else MODEL
     lay, x, ids, gr = _grouped_case(d, T, 41 + T, mode, bm)
     dl = gu.device_layer(lay, d)
     perm = torch.from_numpy(gr.perm).cuda()
+    a = x if tokens else x[torch.from_numpy(gr.perm // d.top_k).long()].contiguous()
     h = torch.empty((T * d.top_k, d.inter), dtype=torch.int16, device="cuda")
-    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.gate_up, m.MOE_EPI_SWIGLU_BF16, x.cuda(), perm,
+    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.gate_up, m.MOE_EPI_SWIGLU_BF16, a.cuda(), perm,
                           torch.from_numpy(gr.offsets).cuda(), torch.from_numpy(gr.block_map).cuda(),
                           torch.tensor([gr.n_tiles], dtype=torch.int32, device="cuda"), gr.block_map.shape[0], None,
-                          T, bm, h)
+                          T, bm, h, a_rows_are_tokens=tokens)
     torch.cuda.synchronize()
     ow = gu.oracle_layer(lay)
     href = oracle.grouped_swiglu(synth.bf16_bits_numpy(x), True, d.top_k, gr.perm, gr.offsets, ow.gate_up, d.hidden,
@@ -242,25 +249,39 @@ def test_grouped_gemm_swiglu(dname, T, mode, bm):
     _h_compare(gu.bits(h), href)
 
 
-@pytest.mark.parametrize("dname,T,mode,bm", [("tiny", 24, "uniform", 128), ("model", 64, "uniform", 128),
-                                             ("model", 700, "zipf", 128), ("model", 130, "uniform", 5)])
-def test_grouped_gemm_scatter(dname, T, mode, bm):
-    say("grouped gemm scatter", dname, T, mode, bm)
+@pytest.mark.parametrize("dname,T,mode,bm,tokens", [("tiny", 24, "uniform", 128, False),
+                                                    ("model", 64, "uniform", 128, False),
+                                                    ("model", 700, "zipf", 128, False),
+                                                    ("model", 130, "uniform", 5, False),
+                                                    ("model", 130, "uniform", 5, True),
+                                                    ("tiny", 300, "zipf", 128, True)])
+def test_grouped_gemm_scatter(dname, T, mode, bm, tokens):
+    """a_rows_are_tokens = 0: rows of h in grouped order (the layer's case);
+    1: rows of a [T][I] gathered per token, a[perm[p] / k]."""
+    say("grouped gemm scatter", dname, T, mode, bm, tokens)
     m = gu.moe()
     d = TINY if dname == "tiny" else MODEL
     lay, x, ids, gr = _grouped_case(d, T, 51 + T, mode, bm)
     dl = gu.device_layer(lay, d)
     ow = gu.oracle_layer(lay)
-    # the oracle's own h as the input of both sides
-    href = oracle.grouped_swiglu(synth.bf16_bits_numpy(x), True, d.top_k, gr.perm, gr.offsets, ow.gate_up, d.hidden,
-                                 d.inter, d.group_size)
+    if tokens:
+        # token-major bf16 rows (any values); the oracle reads them in grouped order
+        a_tok = synth.activations(T, d.inter, 51 + T)
+        a_bits = synth.bf16_bits_numpy(a_tok)
+        href = np.ascontiguousarray(a_bits[gr.perm // d.top_k])
+        a_dev = a_tok.cuda()
+    else:
+        # the oracle's own h as the input of both sides
+        href = oracle.grouped_swiglu(synth.bf16_bits_numpy(x), True, d.top_k, gr.perm, gr.offsets, ow.gate_up,
+                                     d.hidden, d.inter, d.group_size)
+        a_dev = torch.from_numpy(href.view(np.int16)).cuda()
     rw = np.random.default_rng(T).uniform(0.01, 1.0, T * d.top_k).astype(np.float32)
     y = torch.zeros((T, d.hidden), dtype=torch.float32, device="cuda")
-    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.down, m.MOE_EPI_WEIGHTED_SCATTER_F32,
-                          torch.from_numpy(href.view(np.int16)).cuda(), torch.from_numpy(gr.perm).cuda(),
-                          torch.from_numpy(gr.offsets).cuda(), torch.from_numpy(gr.block_map).cuda(),
+    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.down, m.MOE_EPI_WEIGHTED_SCATTER_F32, a_dev,
+                          torch.from_numpy(gr.perm).cuda(), torch.from_numpy(gr.offsets).cuda(),
+                          torch.from_numpy(gr.block_map).cuda(),
                           torch.tensor([gr.n_tiles], dtype=torch.int32, device="cuda"), gr.block_map.shape[0],
-                          torch.from_numpy(rw).cuda(), T, bm, y)
+                          torch.from_numpy(rw).cuda(), T, bm, y, a_rows_are_tokens=tokens)
     torch.cuda.synchronize()
     o = oracle.grouped_down(href, gr.offsets, ow.down, d.hidden, d.inter, d.group_size)
     yref = np.zeros((T, d.hidden))
@@ -269,39 +290,6 @@ def test_grouped_gemm_scatter(dname, T, mode, bm):
         yref += rw.reshape(T, d.top_k)[:, j:j + 1].astype(np.float64) * o[inv[:, j]]
     yg = y.cpu().numpy().astype(np.float64)
     assert np.abs(yg - yref).max() <= 1e-5 * np.abs(yref).max()
-
-
-@pytest.mark.parametrize("dname,T,mode,bm", [("tiny", 24, "uniform", 128), ("model", 64, "uniform", 128),
-                                             ("model", 700, "zipf", 128), ("model", 130, "uniform", 5)])
-def test_grouped_gemm_slots(dname, T, mode, bm):
-    """Weighted slot epilogue: slots[t][j] = fp16(w[t][j] * o) for every routed slot."""
-    say("grouped gemm slots", dname, T, mode, bm)
-    m = gu.moe()
-    d = TINY if dname == "tiny" else MODEL
-    lay, x, ids, gr = _grouped_case(d, T, 71 + T, mode, bm)
-    dl = gu.device_layer(lay, d)
-    ow = gu.oracle_layer(lay)
-    href = oracle.grouped_swiglu(synth.bf16_bits_numpy(x), True, d.top_k, gr.perm, gr.offsets, ow.gate_up, d.hidden,
-                                 d.inter, d.group_size)
-    rw = np.random.default_rng(T).uniform(0.01, 1.0, T * d.top_k).astype(np.float32)
-    k = d.top_k
-    slots = torch.full((T, k + 1, d.hidden), 0x7BFF, dtype=torch.int16, device="cuda")   # fp16 65504 marks "untouched"
-    m.moe_grouped_gemm_q4(gu.to_dims(d), dl.down, m.MOE_EPI_WEIGHTED_SLOTS_F16,
-                          torch.from_numpy(href.view(np.int16)).cuda(), torch.from_numpy(gr.perm).cuda(),
-                          torch.from_numpy(gr.offsets).cuda(), torch.from_numpy(gr.block_map).cuda(),
-                          torch.tensor([gr.n_tiles], dtype=torch.int32, device="cuda"), gr.block_map.shape[0],
-                          torch.from_numpy(rw).cuda(), T, bm, slots)
-    torch.cuda.synchronize()
-    o = oracle.grouped_down(href, gr.offsets, ow.down, d.hidden, d.inter, d.group_size)
-    got = slots.cpu().numpy().view(np.float16).astype(np.float64)
-    ref = np.zeros((T, k, d.hidden))
-    inv = gr.inv_perm.reshape(T, k)
-    for j in range(k):
-        ref[:, j] = rw.reshape(T, k)[:, j:j + 1].astype(np.float64) * o[inv[:, j]]
-    assert np.all(got[:, k] == 65504.0)                       # the shared entry is left alone
-    err = np.abs(got[:, :k] - ref)
-    tol = np.abs(ref) * 2.0 ** -10 + 1e-5 * np.abs(ref).max()  # fp16 rounding of an fp32 result
-    assert np.all(err <= tol), float((err / np.maximum(tol, 1e-30)).max())
 
 
 # ------------------------------------------------------------------ the whole layer
@@ -334,19 +322,36 @@ def test_forward_parity_gemm_forms(hidden, inter, shared, E, k, T):
 
 
 @pytest.mark.parametrize("cfg", ["t4096", "skew16k"])
-def test_forward_parity_large_sampled(cfg):
+def test_forward_parity_full_size(cfg):
+    """The 4096-token layer and the skewed 16384-token layer, every output
+    element against the oracle (the oracle runs on all host threads)."""
     c = synth.CONFIGS[cfg]
-    say("forward sampled", cfg, c.T)
+    say("forward full size", cfg, c.T)
     lay = synth.make_layer(c.dims, c.seed, zipf_bias=c.zipf_bias)
     x = synth.activations(c.T, c.dims.hidden, c.seed)
-    rng = np.random.default_rng(c.seed)
-    tokens = np.sort(rng.choice(c.T, 48, replace=False)).astype(np.int32)
-    tokens[0], tokens[-1] = 0, c.T - 1
-    r = gu.forward_and_check(c.dims, lay, x, tokens=tokens)
+    r = gu.forward_and_check(c.dims, lay, x)
     if c.zipf_bias:
         counts = np.bincount(r["ids"].reshape(-1), minlength=256)
         assert counts.max() > 10 * counts.mean() and (counts == 0).any()
     say("errors", r["errs"])
+
+
+@pytest.mark.parametrize("T,scale", [(1, 64.0), (3, 64.0), (8, 64.0), (512, 64.0), (300, 512.0)])
+def test_forward_parity_large_activations(T, scale):
+    """Activations scaled by 64 and 512 (exact in bf16): expert outputs far
+    past fp16's 65504, the range the down GEMM's fp16 slot values reach only
+    through their per-chunk exponents.  Logits grow with x, so their check
+    against the oracle scales with it (routing is still bit-exact: the
+    protocol shares the GPU logits)."""
+    d = MODEL
+    say("forward large activations T", T, "scale", scale)
+    lay = synth.make_layer(d, 401 + T)
+    x = (synth.activations(T, d.hidden, 401 + T).float() * scale).to(torch.bfloat16)
+    r = gu.forward_and_check(d, lay, x, logit_atol=gu.LOGIT_ATOL * scale)
+    ref = oracle.bf16_to_double(r["ref_bits"])
+    if T >= 8:
+        assert np.abs(ref).max() > 2 * 65504.0   # some slot output exceeds fp16's range
+    say("errors", r["errs"], "max |y|", float(np.abs(ref).max()))
 
 
 def test_forward_parity_max_tokens():
@@ -419,9 +424,10 @@ def test_decode_handover_words():
         x = synth.activations(T, c.dims.hidden, c.seed, step=step % 4).cuda()
         outs.append(m.moe_forward(md, dl, x, workspace=ws).clone())
         torch.cuda.synchronize()
-        words = ws[:1028].view(torch.int32).cpu()
-        assert torch.all(words[:256] == step + 1)      # calls completed, per block
-        assert int(words[256]) == 0                     # timeout word
+        words = ws[:256 + 1024].view(torch.int32).cpu()
+        assert torch.all(words[64:64 + 256] == step + 1)   # calls completed, per block, after the header
+        assert int(words[0]) == 0                          # error word: no hand-over timed out
+        assert m.moe_workspace_errors(ws) == 0
     assert torch.equal(outs[0], outs[4]) and torch.equal(outs[1], outs[5])
 
 
@@ -458,6 +464,18 @@ def test_forward_router_ties(T):
     first = sorted([lo_t, top, hi_t])
     assert list(r["ids"][0][:3]) == first
     say("ids of token 0", list(r["ids"][0]), "ties", first, sorted([a8, eighth, b8]))
+
+
+@pytest.mark.parametrize("T,cfg", [(5, None), (512, "t512"), (700, None), (4096, "skew16k")])
+def test_forward_host_routing_parity(T, cfg):
+    """The variant that takes the expert counts through the host against the
+    oracle (same protocol as moe_forward)."""
+    say("forward host routing vs oracle T", T, cfg)
+    c = synth.CONFIGS[cfg] if cfg else None
+    lay = synth.make_layer(MODEL, 191 + T, zipf_bias=bool(c and c.zipf_bias))
+    x = synth.activations(T, MODEL.hidden, 191 + T)
+    r = gu.forward_and_check(MODEL, lay, x, host_routing=True)
+    say("errors", r["errs"])
 
 
 @pytest.mark.parametrize("T,cfg", [(5, None), (512, "t512"), (700, None), (4096, "skew16k")])
@@ -533,3 +551,44 @@ def test_graph_capture_replays(T):
         assert torch.equal(ids_g, ids_e), rep
         assert torch.equal(y_g, y_e), rep
         del b
+
+
+# ------------------------------------------------------------------ device error word, residency
+
+def test_group_flags_out_of_range_ids():
+    """Caller-supplied ids outside [0, E) are skipped and flagged in the
+    workspace's error word; the in-range slots are grouped as the oracle groups
+    them on their own (counts, and the stable order of the remaining slots)."""
+    say("group out-of-range ids")
+    m = gu.moe()
+    d = MODEL
+    T, bm = 300, 128
+    ids = _ids(T, d.n_experts, d.top_k, "uniform", 9)
+    bad = ids.copy()
+    bad[3, 2], bad[100, 0], bad[299, 7] = -1, d.n_experts, 1 << 20
+    ws = torch.zeros(m.moe_group_workspace_bytes(gu.to_dims(d), T), dtype=torch.uint8, device="cuda")
+    out = m.moe_group(gu.to_dims(d), torch.from_numpy(bad).cuda(), bm, workspace=ws)
+    torch.cuda.synchronize()
+    assert m.moe_workspace_errors(ws, clear=True) == m.MOE_DEVERR_EXPERT_ID
+    assert m.moe_workspace_errors(ws) == 0
+    ok = (bad >= 0) & (bad < d.n_experts)
+    assert np.array_equal(out["counts"].cpu().numpy(), np.bincount(bad[ok], minlength=d.n_experts))
+    inv = out["inv_perm"].cpu().numpy().reshape(T, d.top_k)
+    assert np.all(inv[~ok] == -1)
+    flat = np.flatnonzero(ok.reshape(-1))
+    order = flat[np.argsort(bad.reshape(-1)[flat], kind="stable")]   # expert-major, ascending slot
+    assert np.array_equal(out["perm"].cpu().numpy()[:order.size], order)
+    # a clean call on the same workspace leaves the word clear
+    m.moe_group(gu.to_dims(d), torch.from_numpy(ids).cuda(), bm, workspace=ws)
+    assert m.moe_workspace_errors(ws) == 0
+
+
+def test_fused_residency():
+    """The fused layer's workgroups all fit on the device at once."""
+    m = gu.moe()
+    for T in (1, 2, 4):
+        needed, resident = m.moe_fused_residency(gu.to_dims(MODEL), T)
+        say("fused residency T", T, needed, resident)
+        assert needed == 256 and resident >= needed
+    with pytest.raises(m.MoeError):
+        m.moe_fused_residency(gu.to_dims(MODEL), 5)

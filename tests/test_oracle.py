@@ -268,9 +268,15 @@ def _dense_weights(lw, d):
             "sgu": dq(lw.sh_gate_up, 0, 2 * Is, H), "sdn": dq(lw.sh_down, 0, H, Is)}
 
 
-def test_layer_matches_dense_numpy_reference(oracle_lib):
-    d = TINY
-    lw, x = _tiny_layer(11)
+# shared expert wider and narrower than the routed ones: an exchange of the two
+# intermediate widths anywhere in the oracle fails these
+UNEQUAL = [TINY, oracle.Dims(hidden=128, inter=64, n_experts=16, top_k=4, group_size=64, shared_inter=192),
+           oracle.Dims(hidden=192, inter=128, n_experts=8, top_k=3, group_size=64, shared_inter=64)]
+
+
+@pytest.mark.parametrize("d", UNEQUAL, ids=lambda d: f"I{d.inter}_Is{d.shared_inter}")
+def test_layer_matches_dense_numpy_reference(oracle_lib, d):
+    lw, x = _tiny_layer(11, d=d)
     res = oracle.layer(d, x, lw)
     rids, rw = refs.topk_ref(res["logits"], d.top_k)
     assert np.array_equal(res["ids"], rids)
@@ -280,9 +286,9 @@ def test_layer_matches_dense_numpy_reference(oracle_lib):
     assert np.array_equal(oracle.bf16_to_double(out), out_ref)
 
 
-def test_grouped_form_equals_token_loop_bitwise(oracle_lib):
-    d = TINY
-    lw, x = _tiny_layer(12, T=40)
+@pytest.mark.parametrize("d", UNEQUAL, ids=lambda d: f"I{d.inter}_Is{d.shared_inter}")
+def test_grouped_form_equals_token_loop_bitwise(oracle_lib, d):
+    lw, x = _tiny_layer(12, d=d, T=40)
     res = oracle.layer(d, x, lw)
     ids, w, g = res["ids"], res["w"], res["g"]
     gr = oracle.group(ids, d.n_experts, 16)
