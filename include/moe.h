@@ -267,6 +267,22 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* layer, const uint16_t
                        float* logits_out, int32_t* ids_out, float* w_out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* moe_forward for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The workspace is a device global of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends; nothing is allocated and no allocating library
+ * routine is called.  The caller still passes the inputs and outputs, as for
+ * moe_forward.  T whose moe_workspace_bytes(d, T) exceeds the scratch (for the
+ * model's dims, T above about 600) returns MOE_ERR_WORKSPACE.  Every call on a
+ * device shares that device's scratch: calls that overlap on one device (on
+ * different streams, or from different threads) race and must not be made;
+ * calls on one stream are ordered.  The scratch's device error word has no
+ * reader: use moe_forward with an own workspace to inspect it. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_noalloc(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y,
+                               float* logits_out, int32_t* ids_out, float* w_out, void* stream);
+
 /* The stages of moe_forward, in order.  Grouped path: router GEMM (partial sums over
  * K splits when T is small), top-k + tile histogram, grouping, gate/up grouped GEMM
  * (+ shared expert), down grouped GEMM writing the unweighted slot outputs

@@ -22,6 +22,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_workspace", "moe_forward", "moe_forward_stages", "moe_packed_q4_bytes",
     "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes", "moe_forward_host_routing",
     "moe_gqa_decode_workspace_bytes", "moe_gqa_decode_attention", "moe_workspace_errors", "moe_fused_residency",
+    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "MOE_EPI_SWIGLU_BF16", "MOE_EPI_WEIGHTED_SCATTER_F32", "MOE_DEVERR_HANDOVER_TIMEOUT", "MOE_DEVERR_EXPERT_ID",
     "STAGES", "EXPORTED_SYMBOLS",
 ]
@@ -32,6 +33,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_EPI_SWIGLU_BF16, MOE_EPI_WEIGHTED_SCATTER_F32 = 0, 1
 MOE_DEVERR_HANDOVER_TIMEOUT, MOE_DEVERR_EXPERT_ID = 1, 2
 WORKSPACE_HEADER_BYTES = 256   # the device error word is the first int32
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 STAGES = ("router", "topk", "group", "gate_up", "down", "combine")  # MOE_STAGE_* in order
 MOE_MAT_GATE_UP, MOE_MAT_DOWN, MOE_MAT_SH_GATE_UP, MOE_MAT_SH_DOWN = 0, 1, 2, 3
 
@@ -41,7 +43,7 @@ EXPORTED_SYMBOLS = (
     "moe_forward_stages", "moe_status_str", "moe_last_error_message", "moe_last_hip_error",
     "moe_packed_q4_bytes", "moe_prepack_q4", "moe_host_block_map", "moe_host_routing_bytes",
     "moe_forward_host_routing", "moe_gqa_decode_workspace_bytes", "moe_gqa_decode_attention",
-    "moe_workspace_errors", "moe_fused_residency",
+    "moe_workspace_errors", "moe_fused_residency", "moe_forward_noalloc",
 )
 
 
@@ -114,6 +116,7 @@ def lib():
                                          _I32),
             "moe_workspace_errors": ([_P, _SZ, _I32, ctypes.POINTER(_I32), _P], _I32),
             "moe_fused_residency": ([PD, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], _I32),
+            "moe_forward_noalloc": ([PD, PL, _P, _I32, _P, _P, _P, _P, _P], _I32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(h, name)
@@ -311,6 +314,17 @@ def moe_forward(d, layer: LayerWeights, x: torch.Tensor, y=None, logits_out=None
         workspace = moe_workspace(d, T, x.device)
     _check(lib().moe_forward(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y), _ptr(logits_out),
                              _ptr(ids_out), _ptr(w_out), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def moe_forward_noalloc(d, layer: LayerWeights, x: torch.Tensor, y: torch.Tensor, logits_out=None, ids_out=None,
+                        w_out=None) -> torch.Tensor:
+    """moe_forward on the library's own device scratch: no workspace, and
+    nothing allocated by the call (y and the optional outputs are the
+    caller's)."""
+    T = x.shape[0]
+    _check(lib().moe_forward_noalloc(ctypes.byref(_dims(d)), ctypes.byref(layer.c), _ptr(x), T, _ptr(y),
+                                     _ptr(logits_out), _ptr(ids_out), _ptr(w_out), _stream()))
     return y
 
 

@@ -420,6 +420,58 @@ moe_status moe_forward(const moe_dims* d, const moe_layer* L, const uint16_t* x,
                             MOE_STAGE_COMBINE, stream);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation entry point
+
+// Scratch of moe_forward_noalloc: one whole moe_forward workspace, a device
+// global, so that the call needs no allocation.  Each device the library runs
+// on holds its own copy until the process ends; device globals start
+// zero-filled, which the fused path's hand-over words need before their first
+// call.  In host code `scratch` names a host-side stand-in: its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+moe_status scratch_address(void** out) {
+  int dev = 0;
+  moe_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if ((st = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))) return st;
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_noalloc(const moe_dims* d, const moe_layer* L, const uint16_t* x, int32_t T, uint16_t* y,
+                               float* logits_out, int32_t* ids_out, float* w_out, void* stream) {
+  moe_status st = check_dims(d);
+  if (st) return st;
+  if ((st = check_T(T))) return st;
+  const size_t need = layout(*d, T).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "T=%d needs %zu bytes of scratch; moe_forward_noalloc holds %zu", T, need,
+                static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return moe_forward_stages(d, L, x, T, y, logits_out, ids_out, w_out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                            MOE_STAGE_ROUTER, MOE_STAGE_COMBINE, stream);
+}
+
 moe_status moe_host_block_map(const int32_t* counts, int32_t E, int32_t block_m, int32_t max_tiles, int32_t* offsets,
                               int32_t* block_map, int32_t* n_tiles) {
   if (!counts || !offsets || !block_map || !n_tiles) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");

@@ -94,6 +94,14 @@ def forward_and_check(d, lay: synth.Layer, x_cpu: torch.Tensor, tokens=None, thr
         y = m.moe_forward(md, dl, x, logits_out=logits, ids_out=ids, w_out=wts, workspace=ws)
     torch.cuda.synchronize()
     assert m.moe_workspace_errors(ws) == 0
+    return check_outputs(d, lay, x_cpu, y, logits, ids, wts, tokens=tokens, threads=threads, logit_atol=logit_atol)
+
+
+def check_outputs(d, lay: synth.Layer, x_cpu: torch.Tensor, y, logits, ids, wts, tokens=None, threads: int = 0,
+                  logit_atol: float = LOGIT_ATOL):
+    """The shared-logits parity protocol on outputs the GPU produced (see
+    forward_and_check)."""
+    T = x_cpu.shape[0]
     ow = oracle_layer(lay)
     xb = synth.bf16_bits_numpy(x_cpu)
     o_logits, o_s = oracle.router(xb, ow.router_w, ow.router_bias, ow.shared_gate_w, threads)

@@ -262,3 +262,19 @@ def test_gqa_workspace_and_checks(m):
     assert call(16, 2, 128, FAKE, need, k=ctypes.c_void_p(4100)) == -1       # cache not 16-byte aligned
     assert L.moe_gqa_decode_attention(FAKE, FAKE, FAKE, None, 2, 16, 2, 128, 1000, 0.1, 1, FAKE, FAKE, need,
                                       None) == -1
+
+
+def test_noalloc_limits(m):
+    """The no-allocation entry point refuses, before touching the device, a
+    T whose workspace exceeds its fixed scratch, and bad arguments."""
+    L = m.lib()
+    d = _d(m)
+    q = m._Q4(FAKE, FAKE, FAKE, FAKE)
+    layer = m._Layer(q, q, q, q, FAKE, None, FAKE, FAKE)
+    assert m.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert L.moe_workspace_bytes(d, 512) <= m.NOALLOC_SCRATCH_BYTES < L.moe_workspace_bytes(d, 1024)
+    assert L.moe_forward_noalloc(d, ctypes.byref(layer), FAKE, 1024, FAKE, None, None, None, None) == -3
+    assert "moe_forward_noalloc holds" in L.moe_last_error_message().decode()
+    assert L.moe_forward_noalloc(d, ctypes.byref(layer), FAKE, 0, FAKE, None, None, None, None) == -1
+    assert L.moe_forward_noalloc(_d(m, group_size=32), ctypes.byref(layer), FAKE, 4, FAKE, None, None, None,
+                                 None) == -2
