@@ -211,6 +211,7 @@ def bench_decode(cfg, n_steps, graph_chunk=32):
     e1.record(s_)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    flags = moe.moe_workspace_errors(ws)   # a fused-layer wait that gave up would be flagged here
     gpu_s = e0.elapsed_time(e1) / 1000.0
     bytes_step = cfg.layers * decode_bytes_per_layer(d)
     gbs = n_steps * bytes_step / gpu_s / 1e9
@@ -220,7 +221,8 @@ def bench_decode(cfg, n_steps, graph_chunk=32):
             "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "us_per_step": round(gpu_s * 1e6 / n_steps, 2),
             "us_per_layer": round(gpu_s * 1e6 / n_steps / cfg.layers, 3), "steps": n_steps, "layers": cfg.layers,
             "bytes_per_layer": decode_bytes_per_layer(d), "launch": "HIP graphs of 32 steps",
-            "workload": "decode T=1, 40 layers distinct seeded int4 weights, fresh x per step"}
+            "workload": "decode T=1, 40 layers distinct seeded int4 weights, fresh x per step",
+            "device_error_flags": flags}
 
 
 def bench_routing_ablation(cfg, steps, warmup):
@@ -462,6 +464,81 @@ def profile_stage(cfg, stage, reps):
     log(f"profiled {stage} x{reps} on {cfg.name}, then {reps} copies of 256 MiB")
 
 
+def host_cpu_info() -> dict:
+    """The host the oracle runs on: logical CPUs the OS reports, CPUs this
+    process may run on, and what /proc/cpuinfo and lscpu say about the part."""
+    import subprocess
+    info = {"logical_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        with open("/proc/cpuinfo") as f:
+            first = f.read().split("\n\n")[0]
+        kv = dict((l.split(":", 1)[0].strip(), l.split(":", 1)[1].strip()) for l in first.splitlines() if ":" in l)
+        info.update({"model_name": kv.get("model name"), "cpu_family": kv.get("cpu family"), "model": kv.get("model"),
+                     "stepping": kv.get("stepping")})
+    except OSError:
+        pass
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        kv = dict((l.split(":", 1)[0].strip(), l.split(":", 1)[1].strip()) for l in out.splitlines() if ":" in l)
+        for key, name in (("Socket(s)", "sockets"), ("Core(s) per socket", "cores_per_socket"),
+                          ("Thread(s) per core", "threads_per_core"), ("CPU max MHz", "max_mhz"),
+                          ("Model name", "lscpu_model_name")):
+            if key in kv:
+                info[name] = kv[key]
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return info
+
+
+def cpu_extra_legs(threads: int, decode_steps: int = 8) -> dict:
+    """Two more oracle timings: the 64-token layer on one thread, and batch-1
+    decode over the 40 distinct layers for the first `decode_steps` steps on
+    `threads` threads, scaled to the 256-step run (weights copied to the host
+    outside the timed region)."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    out = {}
+    c1 = synth.CONFIGS["t64"]
+    d = c1.dims
+    od = oracle.Dims(d.hidden, d.inter, d.n_experts, d.top_k, d.group_size, d.shared_inter)
+
+    def ow_of(lay):
+        ln = synth.layer_numpy(lay)
+        return oracle.LayerWeights(ln["gate_up"], ln["down"], ln["sh_gate_up"], ln["sh_down"], ln["router_w"],
+                                   ln["shared_gate_w"], ln["router_bias"])
+    ow = ow_of(synth.make_layer(d, c1.seed, device="cuda"))
+    xb = synth.bf16_bits_numpy(synth.activations(c1.T, d.hidden, c1.seed))
+    log(f"cpu baseline: oracle on the {c1.T}-token layer, one thread")
+    t0 = time.perf_counter()
+    oracle.layer(od, xb, ow, threads=1)
+    secs = time.perf_counter() - t0
+    out["single_thread_t64"] = {"value": round(c1.T / secs, 3), "unit": "tokens/s", "threads": 1,
+                                "seconds": round(secs, 2), "sample": f"all {c1.T} tokens of the 64-token layer"}
+    del ow
+    c4 = synth.CONFIGS["decode"]
+    xs = [synth.bf16_bits_numpy(synth.activations(1, d.hidden, c4.seed, step=s)) for s in range(decode_steps)]
+    log(f"cpu baseline: oracle decode, {decode_steps} steps x {c4.layers} layers, {threads} threads")
+    secs = 0.0
+    for l in range(c4.layers):
+        owl = ow_of(synth.make_layer(d, c4.seed, layer=l, device="cuda"))
+        t0 = time.perf_counter()
+        for s in range(decode_steps):
+            oracle.layer(od, xs[s], owl, threads=threads)
+        secs += time.perf_counter() - t0
+        del owl
+        torch.cuda.empty_cache()
+    per_step = secs / decode_steps
+    out["decode_40_layers"] = {"us_per_step": round(per_step * 1e6, 1),
+                               "tokens_per_s": round(1.0 / per_step, 4), "threads": threads,
+                               "sample": f"the first {decode_steps} of 256 steps x {c4.layers} layers, "
+                                         f"scaled x{256 // decode_steps} to the 256-step run "
+                                         f"({secs * 256 / decode_steps:.1f} s)",
+                               "seconds_measured": round(secs, 2)}
+    return out
+
+
 def cpu_baseline(res, sample, threads, min_secs=10.0, max_passes=8):
     """The oracle, as it stands, on `sample` tokens of the same workload; also
     cross-checks those tokens' GPU outputs (shared-logits protocol)."""
@@ -500,14 +577,11 @@ def cpu_baseline(res, sample, threads, min_secs=10.0, max_passes=8):
     max_rel = float(np.abs(g - o).max() / np.abs(o).max())
     l1_rel = float(np.abs(g - o).sum() / np.abs(o).sum())
     log(f"cpu baseline: {secs:.2f} s; parity max_rel {max_rel:.2e} l1_rel {l1_rel:.2e} ids_equal {ids_equal}")
-    cpu_model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
-    except OSError:
-        pass
+    host = host_cpu_info()
     return ({"value": round(passes * sample / secs, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-             "cpu_model": cpu_model,
+             "cores_note": "threads the oracle ran on: the host's CPU share for one GPU (at most 16), "
+                           "not its core count (see host)",
+             "host": host, "cpu_model": host.get("model_name"),
              "sample": f"{sample} of the {cfg.T} tokens of the same layer (router, top-k, experts incl. "
                        f"dequantisation of the experts they touch, combine), {passes} pass(es), {secs:.1f} s"},
             {"tokens": sample, "logit_max_abs_err": logit_err, "ids_equal_given_gpu_logits": ids_equal,
@@ -527,8 +601,11 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the routing ablation and the small-T sweep")
     ap.add_argument("--cpu-sample", type=int, default=4096)
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-decode-steps", type=int, default=8,
+                    help="decode steps the oracle's 40-layer decode timing covers (scaled to 256)")
     ap.add_argument("--profile-stage", default=None,
-                    help="profiling run: one stage repeated, no JSON line (gqa_decode: the attention leg alone)")
+                    help="profiling run: one stage repeated, no JSON line (gqa_decode: the attention leg alone; "
+                         "decode: the 40-layer decode leg alone)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -545,6 +622,15 @@ def main():
     if args.profile_stage == "gqa_decode":
         print(json.dumps({"gqa_decode_attention": bench_gqa_decode(reps=args.steps)}), flush=True)
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")   # counter calibration, as profile_stage
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        return
+    if args.profile_stage == "decode":
+        # the 40-layer decode leg alone (args.steps steps), then the counter-calibration copies
+        print(json.dumps({"decode": bench_decode(synth.CONFIGS["decode"], args.steps, graph_chunk=8)}), flush=True)
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
@@ -603,8 +689,10 @@ def main():
             out["skewed_routing"] = bench_skewed(synth.CONFIGS["skew16k"])
         out["gqa_decode_attention"] = bench_gqa_decode()
     if not args.no_cpu_baseline:
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)) or 1)
         out["cpu_baseline"], out["parity_sample"] = cpu_baseline(res, args.cpu_sample, threads)
+        if not args.no_extras:
+            out["cpu_baseline"].update(cpu_extra_legs(threads, args.cpu_decode_steps))
     print(json.dumps(out), flush=True)
 
 

@@ -12,13 +12,14 @@
 //      row(s), the shared expert's gate/up rows of this wave's column pair and
 //      its down rows for this wave's output row;
 //   B. router dot products (fp32 weights) of every token -> logit words
-//   C. shared expert SwiGLU column pair, every token    -> h words of slot k
 //   D. every block polls the logit words until all carry this call's tag and
 //      recomputes every token's top-k itself (all waves, lower expert index
 //      on ties), so the routing decision needs no second round trip;
 //   E. issue the routed experts' gate/up rows of this wave's (token, slot,
 //      column pair) task and the down rows of every token's experts for this
 //      wave's output row;
+//   C. while those rows are in flight: shared expert SwiGLU column pair,
+//      every token                                      -> h words of slot k
 //   F. routed SwiGLU column pairs                       -> h words of slot j
 //   G. poll the h words; down GEMV over each token's k+1 slots with the
 //      weighted combine in registers, slot order, shared expert last -> y.
@@ -310,14 +311,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
     }
   }
 
-  // ---- C: shared expert column pair, every token
-  if (has_sh) {
+  // ---- C: shared expert column pair, every token.  In the one-token form
+  // with hidden <= 2048 it runs after the routing decision, while the routed
+  // rows are in flight (it needs no routing, and before the logit poll it
+  // would only delay the routing decision); the wider and multi-token forms
+  // have no registers to hold its rows that long, and run it here.
+  constexpr bool kLateShared = TM == 1 && KCG == 1;
+  if constexpr (!kLateShared) {
+    if (has_sh) {
 #pragma unroll
-    for (int t = 0; t < TM; ++t)
-      if (t < T) {
-        const uint32_t hv = swiglu_pair<KCG>(sh, xv[t], H, lane);
-        if (lane == 0) put(hw + (static_cast<int64_t>(t) * (k + 1) + k) * hp + p_sh, tagged(tag, hv));
-      }
+      for (int t = 0; t < TM; ++t)
+        if (t < T) {
+          const uint32_t hv = swiglu_pair<KCG>(sh, xv[t], H, lane);
+          if (lane == 0) put(hw + (static_cast<int64_t>(t) * (k + 1) + k) * hp + p_sh, tagged(tag, hv));
+        }
+    }
   }
 
   // ---- D: routing decision of every token (every block)
@@ -419,8 +427,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
           if (n < H && t < T && j < k) load_dn<KCD>(a.dn, s_e[t][j], I, n, H, lane, dr[i][t * KMAX + j]);
     }
   };
-  bool down_issued = false;
-  for (int q0 = gw; q0 < n_tasks; q0 += NW * kDecTasks<KCG>) {
+  // Every wave runs the first round, even without a task: there, right after
+  // requesting its first gate/up rows, it requests its routed down rows (with
+  // hidden <= 2048) and computes the late shared pair while the rows are in
+  // flight.
+  bool first = true;
+  for (int q0 = gw;; q0 += NW * kDecTasks<KCG>) {
     GuPair<KCG> ru[kDecTasks<KCG>];
     uint4 xq[TM == 1 ? 1 : kDecTasks<KCG>][KCG][4];   // the task's token (one token: xv)
 #pragma unroll
@@ -440,9 +452,15 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
         }
       }
     }
-    if (KCG == 1 && !down_issued) {
-      load_down();
-      down_issued = true;
+    if (first) {
+      if constexpr (KCG == 1) load_down();
+      if constexpr (kLateShared) {
+        if (has_sh) {   // one token (TM == 1)
+          const uint32_t hv = swiglu_pair<KCG>(sh, xv[0], H, lane);
+          if (lane == 0) put(hw + static_cast<int64_t>(k) * hp + p_sh, tagged(tag, hv));
+        }
+      }
+      first = false;
     }
 #pragma unroll
     for (int u = 0; u < kDecTasks<KCG>; ++u) {
@@ -457,8 +475,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_layer(DecArgs a) {
         if (lane == 0) put(hw + (static_cast<int64_t>(slot) + t) * hp + q % ip, tagged(tag, hv));
       }
     }
+    if (q0 + NW * kDecTasks<KCG> >= n_tasks) break;
   }
-  if (!down_issued) load_down();
+  if constexpr (KCG != 1) load_down();
 
   // ---- G: all of h, then down GEMV and combine, every token
   constexpr int kHWords = TM * (KMAX + 1) * 256 * KCD;   // T (k + 1) slots of at most 512 KCD columns

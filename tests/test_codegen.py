@@ -52,3 +52,30 @@ def test_k_loops_issue_only_direct_lds_loads(tmp_path):
         for h, v in k_loops.items():
             others = [o for o in v if o != "lds-load"]
             assert not others, (k, h, others)
+
+
+@pytest.mark.skipif(shutil.which("/opt/rocm/bin/hipcc") is None and shutil.which("hipcc") is None,
+                    reason="hipcc not available")
+def test_fused_layer_keeps_its_arrays_in_registers(tmp_path):
+    """The fused 1-4-token layer holds x, the prefetched weight rows and the
+    partial sums in register arrays.  A code change can silently turn them into
+    per-lane stack memory (a lambda capturing them by reference that is not
+    inlined, a helper with too many call sites): the layer then ran ~60%
+    slower.  Every form but the widest (k > 8 with hidden and inter both at
+    their largest) must use no private segment."""
+    from sparse_moe_softmax_amd import build as B
+    asm = tmp_path / "decode.s"
+    cmd = [B.HIPCC, *B.FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, "decode.hip"), "-o", str(asm)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    s = asm.read_text()
+    meta = re.findall(r"\.name:\s+(_ZN3moe14k_decode_layerILi(\d)ELi(\d)ELi(\d+)ELi(\d)EEEvNS_7DecArgsE)"
+                      r"[\s\S]*?\.private_segment_fixed_size:\s+(\d+)", s)
+    if not meta:   # metadata keys in the other order
+        meta = re.findall(r"\.private_segment_fixed_size:\s+(\d+)[\s\S]*?\.name:\s+"
+                          r"(_ZN3moe14k_decode_layerILi(\d)ELi(\d)ELi(\d+)ELi(\d)EEEvNS_7DecArgsE)", s)
+        meta = [(n, a, b, c, d, p) for p, n, a, b, c, d in meta]
+    assert len(meta) == 9, meta
+    for name, kcg, kcd, kmax, tm, priv in meta:
+        if (kcg, kcd, kmax) == ("2", "2", "16"):
+            continue
+        assert int(priv) == 0, (name, priv)
