@@ -211,7 +211,7 @@ typedef enum moe_epilogue {
  * perm/offsets/block_map/n_tiles as produced by moe_group() with the same
  * block_m (the kernels trust them: expert ids in [0, E), rows inside [0, T*k));
  * 1 <= block_m <= moe_block_m(). */
-moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
+moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, int32_t epi /* moe_epilogue */, const uint16_t* a,
                                int32_t a_rows_are_tokens, const int32_t* perm, const int32_t* offsets,
                                const int32_t* block_map, const int32_t* n_tiles, int32_t max_tiles,
                                const float* row_weight, int32_t T, int32_t block_m, void* out, void* stream);
@@ -363,8 +363,9 @@ moe_status moe_gqa_decode_attention(const uint16_t* q, const uint16_t* k_cache, 
                                     float scale, int32_t pack_heads, uint16_t* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
-/* Human-readable name of a status; message of the last failed check on this thread. */
-const char* moe_status_str(moe_status s);
+/* Human-readable name of a status ("MOE_ERR_UNKNOWN" for a value that is none);
+ * message of the last failed check on this thread. */
+const char* moe_status_str(int32_t status);
 const char* moe_last_error_message(void);
 /* hipError_t of the last failed launch on this thread (0 if none). */
 int32_t moe_last_hip_error(void);

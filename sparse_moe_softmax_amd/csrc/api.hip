@@ -169,7 +169,7 @@ int32_t moe_max_tiles(int32_t T, int32_t top_k, int32_t n_experts, int32_t block
   return static_cast<int32_t>(div_up(static_cast<int64_t>(T) * top_k, block_m) + n_experts);
 }
 
-const char* moe_status_str(moe_status s) {
+const char* moe_status_str(int32_t s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
@@ -276,7 +276,7 @@ moe_status moe_group(const moe_dims* d, const int32_t* ids, int32_t T, int32_t b
                    "grouping");
 }
 
-moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue epi, const uint16_t* a,
+moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, int32_t epi, const uint16_t* a,
                                int32_t a_rows_are_tokens, const int32_t* perm, const int32_t* offsets,
                                const int32_t* block_map, const int32_t* n_tiles, int32_t max_tiles,
                                const float* row_weight, int32_t T, int32_t block_m, void* out, void* stream) {
@@ -308,7 +308,7 @@ moe_status moe_grouped_gemm_q4(const moe_dims* d, const moe_q4* w, moe_epilogue 
                                          static_cast<float*>(out), s),
                      "grouped gemm (scatter)");
   }
-  return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", static_cast<int>(epi));
+  return fail(MOE_ERR_INVALID_ARG, "unknown epilogue %d", epi);
 }
 
 size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max) {
