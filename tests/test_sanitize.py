@@ -27,7 +27,6 @@ SAN = "address,undefined"
 HIPCC = "/opt/rocm/bin/hipcc"
 CLANG = "/opt/rocm/llvm/bin/clang++"
 CSRC = os.path.join(ROOT, "sparse_moe_softmax_amd", "csrc")
-SOURCES = ["api", "route", "group", "gemm", "decode", "attn"]
 
 
 def _digest(paths, extra=""):
@@ -66,7 +65,8 @@ def test_oracle_under_sanitizers():
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANG)), reason="ROCm compilers not available")
 def test_abi_host_code_under_sanitizers():
     os.makedirs(OUT, exist_ok=True)
-    hip = [os.path.join(CSRC, f + ".hip") for f in SOURCES]
+    from sparse_moe_softmax_amd import build as B
+    hip = [os.path.join(CSRC, f) for f in B.SOURCES]
     hdrs = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hpp")]
     drv = os.path.join(ROOT, "tests", "sanitize", "abi_driver.cpp")
     tag = _digest(hip + hdrs + [drv, os.path.join(ROOT, "include", "moe.h")])
