@@ -255,7 +255,7 @@ moe_status moe_fused_residency(const moe_dims* d, int32_t T, int32_t* needed, in
  * the shared expert's tiles run in the same GEMM launches.  The down GEMM stores every
  * routed slot's output and the shared expert's output unweighted, as fp16
  * values with a power-of-two exponent per 64 columns (fp32's range; fp16's
- * 11-bit precision for every value within 2^24 of its 64-column chunk's
+ * 11-bit precision for every value within 2^28 of its 64-column chunk's
  * largest), and a final pass multiplies each of a token's k+1 entries by its
  * routing weight (the shared one by the gate) and sums them in slot order in
  * fp32, so y is bitwise reproducible.  The fused path keeps everything in

@@ -43,11 +43,11 @@
 //   SLOTS  : the unweighted output o of slot j of a token (routed slots
 //            j < k, the shared expert's slot k), token-major [T][k+1][H], as
 //            fp16 with a power-of-two exponent per (slot row, 64 columns):
-//            slot = fp16(o * 2^-e), e >= 0 the smallest that keeps the
-//            64-value chunk below 2^15, so the range is fp32's and every value
-//            keeps fp16's 11-bit precision unless it lies 2^24 below its
-//            chunk's largest.  The combine weights and sums them afterwards in
-//            a fixed order.  No atomics.
+//            slot = fp16(o * 2^-e), e chosen so that the 64-value chunk's
+//            largest magnitude lies in [2^14, 2^15): the range is fp32's and
+//            every value within 2^28 of its chunk's largest keeps fp16's
+//            11-bit precision.  The combine weights and sums them afterwards
+//            in a fixed order.  No atomics.
 //
 // Launch order is XCD-aware: consecutive workgroup ids go round-robin to the 8
 // XCDs, so ids are mapped such that all column slices of one tile share an XCD
@@ -77,18 +77,20 @@ static_assert(kRingBytes % 256 == 0, "ring alignment");
 
 enum { kSwiglu = 0, kScatter = 1, kSlots = 2 };
 
-// Slot epilogue staging: a wave's 32 x 64 fp32 sub-tile, rows padded to 72 floats.
-constexpr int kSlotRowFloats = 72;
-constexpr int kSlotStageBytes = 32 * kSlotRowFloats * 4;
+// Slot epilogue staging: a wave's 32 x 64 fp16 sub-tile, rows padded to 144 bytes.
+constexpr int kSlotRowBytes = 144;   // 64 fp16 + 16 B pad
+constexpr int kSlotStageBytes = 32 * kSlotRowBytes;
 static_assert(4 * kSlotStageBytes <= kRingBytes, "slot staging fits the ring");
 
-// Exponent e >= 0 of a slot chunk whose largest magnitude is mx: the smallest
-// with mx * 2^-e < 2^15, so that fp16 rounding of every scaled value stays
-// finite (fp16's largest finite value is 65504).  Integer work on the bits:
-// floor(log2(mx)) = biased exponent - 127 for normal mx; 0 for mx < 2^15.
+// Exponent e of a slot chunk whose largest magnitude is mx: mx * 2^-e lies in
+// [2^14, 2^15) (for 2^-96 <= mx < 2^128), so every scaled value is finite in
+// fp16 (largest finite 65504) and every value within 2^28 of mx is an fp16
+// normal with its 11-bit significand.  Integer work on the bits:
+// floor(log2(mx)) = biased exponent - 127 for normal mx.  e is kept in
+// [-110, 113] so that 2^-e and 2^e are normal floats; stored as int8.
 __device__ inline int slot_exponent(float mx) {
   const int fl = static_cast<int>((__float_as_uint(mx) >> 23) & 255u) - 127;
-  return max(0, fl - 14);
+  return min(113, max(-110, fl - 14));
 }
 // Two floats -> two fp16 (round to nearest even), low half first.
 __device__ inline uint32_t pack_f16x2(float lo, float hi) {
@@ -146,7 +148,18 @@ struct Tile {
 // offsets 32g+8s .. 32g+8s+7 for both operands (a consistent permutation of K).
 // A fragment: row lane%32 of the sub-tile; B fragment: weight row (column)
 // lane%32 of the column group; C: acc[m][c][j] holds row 8(j/4) + 4g + (j%4),
-// column lane%32.
+// column lane%32.  The two operand fragments have the same lane layout, so
+// swapping them gives the transposed product: the SLOTS epilogue takes it that
+// way (acc[m][c][j] then holds row lane%32, column 8(j/4) + 4g + (j%4)), so
+// that a lane owns 32 values of one output row.
+template <int MODE>
+__device__ __forceinline__ f32x16 mma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (MODE == kSlots)
+    return mfma32(b, a, c);
+  else
+    return mfma32(a, b, c);
+}
+
 template <int MODE, int MT, int KS>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsigned char* ring,
                                           int64_t* s_drow, float* s_wt) {
@@ -298,7 +311,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[q & 1][m], bq[q & 1][c], acc[m][c]);
+        for (int m = 0; m < MT; ++m) acc[m][c] = mma<MODE>(af[q & 1][m], bq[q & 1][c], acc[m][c]);
         if (q + 1 < 4 * KS) bq[(q + 1) & 1][c] = dq(raw[nu], c, nks);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -333,7 +346,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][c] = mfma32(af[ks & 1][m], bcur[c][ks], acc[m][c]);
+        for (int m = 0; m < MT; ++m) acc[m][c] = mma<MODE>(af[ks & 1][m], bcur[c][ks], acc[m][c]);
         if (more) bnext[c][ks] = dq(raw, c, ks);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -422,47 +435,44 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
       __builtin_amdgcn_wave_barrier();
     }
   } else if (MODE == kSlots) {
-    // Each wave stages a 32-row sub-tile of its 64 columns as fp32 (rows of 72
-    // floats: the two lane halves of a store hit disjoint banks), then 8 lanes
-    // per row take the row's largest magnitude, pick the exponent e and store
-    // fp16(o * 2^-e) as 16 contiguous bytes per lane, lane 0 of the 8 the
-    // exponent byte.
+    // The products are transposed here (see mma): a lane owns 32 values of
+    // row `col` of the sub-tile, the 4-column runs 8i + 4g .. 8i + 4g + 3 of
+    // the wave's 64 columns.  The row's largest magnitude is the lane's own
+    // maximum combined with that of lane ^ 32 (the other runs).  The values
+    // scaled by 2^-e go to fp16 and are staged as rows of 64 fp16 (+16 B pad)
+    // so that stores are 16 contiguous bytes per lane; lane g == 0 stores the
+    // row's exponent byte.
     uint16_t* out = static_cast<uint16_t*>(g.out[0]);   // [T][k+1][H] fp16
     const int H = g.H;
-    const int n_chunks = H >> 6;
-    float* stf = reinterpret_cast<float*>(ring + wave * kSlotStageBytes);
+    const int chunk = t.n0 >> 6, n_chunks = H >> 6;
+    unsigned char* st16 = ring + wave * kSlotStageBytes;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
+      float mx = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = (j >> 2) * 8 + gq * 4 + (j & 3);
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) stf[r * kSlotRowFloats + c * 32 + col] = acc[m][c][j];
-      }
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(acc[m][c][j]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const int e = slot_exponent(mx);
+      const float sc = __int_as_float((127 - e) << 23);   // 2^-e, exact scaling
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint2 v = {pack_f16x2(acc[m][c][4 * i] * sc, acc[m][c][4 * i + 1] * sc),
+                           pack_f16x2(acc[m][c][4 * i + 2] * sc, acc[m][c][4 * i + 3] * sc)};
+          *reinterpret_cast<uint2*>(st16 + col * kSlotRowBytes + (c * 32 + 8 * i + 4 * gq) * 2) = v;
+        }
+      if (gq == 0 && m * 32 + col < rows)
+        g.slot_exp[s_drow[m * 32 + col] * n_chunks + chunk] = static_cast<uint8_t>(e & 255);
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
         const int r = part * 8 + (lane >> 3), pc = lane & 7;
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(stf + r * kSlotRowFloats + pc * 8);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(stf + r * kSlotRowFloats + pc * 8 + 4);
-        float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                         fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
-        // largest over the row's 8 lanes: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0xB1, 0xF, 0xF, false)));
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x4E, 0xF, 0xF, false)));
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(mx), 0x141, 0xF, 0xF, false)));
-        const int e = slot_exponent(mx);
-        const float sc = __int_as_float((127 - e) << 23);   // 2^-e, exact scaling
-        uint4 o;
-        o.x = pack_f16x2(v0.x * sc, v0.y * sc);
-        o.y = pack_f16x2(v0.z * sc, v0.w * sc);
-        o.z = pack_f16x2(v1.x * sc, v1.y * sc);
-        o.w = pack_f16x2(v1.z * sc, v1.w * sc);
-        if (m * 32 + r < rows) {
-          const int64_t drow = s_drow[m * 32 + r];
-          *reinterpret_cast<uint4*>(out + drow * H + t.n0 + pc * 8) = o;
-          if (pc == 0) g.slot_exp[drow * n_chunks + (t.n0 >> 6)] = static_cast<uint8_t>(e);
-        }
+        const uint4 v = *reinterpret_cast<const uint4*>(st16 + r * kSlotRowBytes + pc * 16);
+        if (m * 32 + r < rows)
+          *reinterpret_cast<uint4*>(out + s_drow[m * 32 + r] * H + t.n0 + pc * 8) = v;
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -730,7 +740,8 @@ hipError_t launch_prepack_q4(const moe_dims& d, int matrix, const moe_q4& w, int
 // (fp16 slot values and their chunk exponents as the slot epilogue wrote
 // them), summed in fp32 in slot order (shared expert last); w or gate NULL =
 // weights of 1.  The weight and 2^e are multiplied first (exact: a power-of-two
-// scaling), so each term is the single rounding of w * o.  8 columns per
+// scaling, unless w * 2^e falls below fp32's normal range, which needs chunks
+// near 2^-96), so each term is the single rounding of w * o.  8 columns per
 // thread.  With k known at compile time (K > 0) all k + 1 slot vectors and
 // exponents are requested before the sum, so a thread waits for one memory
 // round trip, not k + 1; K = 0 takes k at run time.
@@ -749,8 +760,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
   const uint16_t* src = slots + t * (k + 1) * H + c8;
   const uint8_t* esrc = slot_exp + t * (k + 1) * n_chunks + (c8 >> 6);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto add = [&](const uint4& v, float wj, uint32_t e) {
-    const float we = wj * __uint_as_float((127u + e) << 23);   // w * 2^e
+  auto add = [&](const uint4& v, float wj, int e) {
+    const float we = wj * __int_as_float((127 + e) << 23);   // w * 2^e
     const f16x2 p[4] = {__builtin_bit_cast(f16x2, v.x), __builtin_bit_cast(f16x2, v.y),
                         __builtin_bit_cast(f16x2, v.z), __builtin_bit_cast(f16x2, v.w)};
 #pragma unroll
@@ -761,11 +772,11 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
   };
   if constexpr (K > 0) {
     uint4 v[K + 1];
-    uint32_t e[K + 1];
+    int e[K + 1];
 #pragma unroll
     for (int j = 0; j <= K; ++j) {
       v[j] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
-      e[j] = esrc[j * n_chunks];
+      e[j] = static_cast<int8_t>(esrc[j * n_chunks]);
     }
     float wj[K + 1];
 #pragma unroll
@@ -776,7 +787,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ sl
   } else {
     for (int j = 0; j <= k; ++j) {
       const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * H);
-      add(v, j == k ? (gate ? gate[t] : 1.0f) : (w ? w[t * k + j] : 1.0f), esrc[j * n_chunks]);
+      add(v, j == k ? (gate ? gate[t] : 1.0f) : (w ? w[t * k + j] : 1.0f), static_cast<int8_t>(esrc[j * n_chunks]));
     }
   }
   uint4 o;

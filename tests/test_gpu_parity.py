@@ -336,21 +336,25 @@ def test_forward_parity_full_size(cfg):
     say("errors", r["errs"])
 
 
-@pytest.mark.parametrize("T,scale", [(1, 64.0), (3, 64.0), (8, 64.0), (512, 64.0), (300, 512.0)])
-def test_forward_parity_large_activations(T, scale):
-    """Activations scaled by 64 and 512 (exact in bf16): expert outputs far
-    past fp16's 65504, the range the down GEMM's fp16 slot values reach only
-    through their per-chunk exponents.  Logits grow with x, so their check
+@pytest.mark.parametrize("T,scale", [(1, 64.0), (3, 64.0), (8, 64.0), (512, 64.0), (300, 512.0),
+                                     (3, 2.0 ** -12), (300, 2.0 ** -12)])
+def test_forward_parity_activation_scale(T, scale):
+    """Activations scaled by powers of two (exact in bf16).  By 64 and 512 the
+    expert outputs go far past fp16's 65504; by 2^-12 they fall to ~2^-24,
+    fp16's subnormal range.  The down GEMM's fp16 slot values cover both only
+    through their per-chunk exponents.  Logits scale with x, so their check
     against the oracle scales with it (routing is still bit-exact: the
     protocol shares the GPU logits)."""
     d = MODEL
-    say("forward large activations T", T, "scale", scale)
+    say("forward activation scale T", T, "scale", scale)
     lay = synth.make_layer(d, 401 + T)
     x = (synth.activations(T, d.hidden, 401 + T).float() * scale).to(torch.bfloat16)
     r = gu.forward_and_check(d, lay, x, logit_atol=gu.LOGIT_ATOL * scale)
     ref = oracle.bf16_to_double(r["ref_bits"])
-    if T >= 8:
+    if T >= 8 and scale > 1:
         assert np.abs(ref).max() > 2 * 65504.0   # some slot output exceeds fp16's range
+    if scale < 1:
+        assert np.abs(ref).max() < 2.0 ** -14    # every output is below fp16's normal range
     say("errors", r["errs"], "max |y|", float(np.abs(ref).max()))
 
 
