@@ -10,17 +10,29 @@
 // instead of loading it once per query head.
 //
 // Here one workgroup owns (sequence, key/value head, range of positions) and
-// all the group's query heads (at most 8).  It stages 32 key and value rows at
-// a time in LDS with 16-byte loads (the next 32 rows are loaded into registers
-// meanwhile), scores every staged row against every query head (lane =
-// (position, one of the wave's two heads): one dot product per lane), keeps a
-// running maximum and sum per head (online softmax), and accumulates the
-// weighted value rows in fp32 registers (lane = 8 columns x a group of heads;
-// the four waves take every fourth position and are added at the end).  Each range leaves its (maximum, sum, unnormalised output) in
-// the workspace; k_gqa_merge combines a head's ranges in range order, so the
-// result does not depend on scheduling.  With one query head per workgroup
-// (pack_heads == 0) the same kernel reads each key/value row once per query
-// head: the unpacked form the packing is measured against.
+// all the group's query heads (at most 8).  Its eight waves work independently:
+// wave w takes the 16-position stages w, w + 8, ... of the range.  A wave
+// brings a stage's 16 key and 16 value rows into its own LDS slots with
+// direct-to-LDS loads (16-byte chunks XOR-swizzled by row, so that the
+// fragment reads below are conflict-free), the next stage's keys being
+// requested as soon as the current scores are formed and its values as soon
+// as the current values are used; no workgroup barrier is needed until the
+// end.  Scores are one v_mfma_f32_16x16x32_bf16 chain per stage (16 positions
+// x 16 query-head columns, the key rows as the first operand and the query
+// rows, held in registers, as the second; columns past the group are zero).
+// An online softmax keeps each head's running maximum and sum.  The weighted
+// value sum is a second MFMA chain, v_mfma_f32_16x16x16_bf16 per 16 value
+// columns, computing the transposed output (value columns x heads): the score
+// registers already hold the probabilities in the layout of its second
+// operand, split exactly into a bf16 high part and a bf16 remainder (two
+// MFMAs, so they keep 16 significant bits), and the first operand is the
+// value rows read column-wise from LDS.  At the end the waves' states
+// are combined in wave order, and each range leaves its (maximum, sum,
+// unnormalised output) in the workspace; k_gqa_merge combines a head's ranges
+// in range order, so the result does not depend on scheduling.  With one
+// query head per workgroup (pack_heads == 0) the same kernel reads each
+// key/value row once per query head: the unpacked form the packing is
+// measured against.
 
 #include "internal.hpp"
 #include "attn.hpp"
@@ -29,20 +41,41 @@ namespace moe {
 
 namespace {
 
-constexpr int kAtSub = 32;        // positions staged per step: one per lane of a half wave
-constexpr int kAtThreads = 256;
+constexpr int kAtPos = 16;        // positions per stage: the rows of one 16x16x32 MFMA
+constexpr int kAtWaves = 8;
+constexpr int kAtThreads = 64 * kAtWaves;
 constexpr int kMgThreads = 256;   // merge
 constexpr int kAtGroup = 8;       // query heads per workgroup at most
-constexpr int kAtTarget = 512;    // workgroups wanted per launch (three fit a CU: 38 KB LDS, 148 VGPRs)
+constexpr int kAtTarget = 2048 / kAtWaves;   // workgroups wanted per launch: eight waves per CU (16 KB of LDS each)
+
+template <int D>
+struct AtGeom {
+  static constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kSlot = kAtPos * kRowBytes;    // the key (or value) rows of one stage
+  static constexpr int kLoads = kSlot / 1024;         // 1 KB direct loads per slot and wave
+  // XOR key of row r: rows sharing a 256-byte bank line get distinct keys
+  static constexpr int kShift = kChunks >= 16 ? 0 : 1;
+  static constexpr int kMask = (kChunks >= 16 ? 16 : kChunks) - 1;
+  static_assert(kSlot % 1024 == 0, "whole 1 KB loads");
+};
+// Physical 16-byte chunk of logical chunk c in row r of a slot (and back: the
+// XOR is its own inverse).  The 16 rows of an MFMA fragment read, and the
+// chunks of one row read by the value lanes, fall in distinct bank groups.
+template <int D>
+__device__ inline int at_chunk(int r, int c) {
+  return c ^ ((r >> AtGeom<D>::kShift) & AtGeom<D>::kMask);
+}
 
 template <int D>
 struct AttnLds {
-  uint32_t q[kAtGroup][D / 2];          // query rows, bf16 pairs
-  uint16_t k[kAtSub][D + 8];            // key rows; +16 bytes per row: rows start 4 banks apart
-  uint16_t v[kAtSub][D];                // value rows
-  float p[kAtSub][kAtGroup];            // exp(score - running max), position-major
-  float alpha[kAtGroup];                // rescale of the running output for this step
+  unsigned char kv[kAtWaves][2][AtGeom<D>::kSlot];   // per wave: key slot, value slot
+  float fac[kAtGroup][kAtWaves];                     // end: each wave's factor e^(m_w - M) per head
 };
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+__device__ inline f32x4 mfma16k16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
 __device__ inline float wave_max64(float v) {
 #pragma unroll
@@ -55,21 +88,20 @@ __device__ inline float wave_sum64(float v) {
   return v;
 }
 
-__device__ inline float dot8(const uint4 a, const uint4 b, float c) {
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), c, false);
-  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), c, false);
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), c, false);
-}
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS reads have returned before a
+// direct load may overwrite what they read.
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 template <int D>
-__global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ kc,
-                                                            const uint16_t* __restrict__ vc,
-                                                            const int32_t* __restrict__ lens, int Hq, int Hkv, int S,
-                                                            int gw, int rows_per_split, int n_splits, float scale,
-                                                            float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) AttnLds<D> sm;
+__global__ __launch_bounds__(kAtThreads, 8 / kAtWaves) void k_gqa_partial(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ kc,
+                                                               const uint16_t* __restrict__ vc,
+                                                               const int32_t* __restrict__ lens, int Hq, int Hkv,
+                                                               int S, int gw, int rows_per_split, int n_splits,
+                                                               float scale, float* __restrict__ part_o,
+                                                               float* __restrict__ part_ml) {
+  using G = AtGeom<D>;
+  __shared__ __attribute__((aligned(1024))) AttnLds<D> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, b = blockIdx.z;
   const int h0 = blockIdx.y * gw;                 // first query head of this workgroup
@@ -78,162 +110,175 @@ __global__ __launch_bounds__(kAtThreads) void k_gqa_partial(const uint16_t* __re
   const int start = split * rows_per_split;
   if (start >= L) return;                         // the merge reads only ranges below L
   const int end = min(start + rows_per_split, L);
+  const int n_st = (end - start + kAtPos - 1) / kAtPos;
+  const int my_st = n_st > wave ? (n_st - wave + kAtWaves - 1) / kAtWaves : 0;   // stages wave, wave + kAtWaves, ...
 
-  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(q);
-  for (int i = tid; i < kAtGroup * (D / 2); i += kAtThreads) {
-    const int g = i / (D / 2), c = i % (D / 2);
-    sm.q[g][c] = g < gw ? q32[((static_cast<int64_t>(b) * Hq + h0 + g) * D) / 2 + c] : 0u;
+  // score roles: lane = (position row lane % 16 of the key fragment, query
+  // head column lane % 16 of the query fragment and of the scores), lane
+  // group qg = lane / 16 covering K offsets 8 qg .. 8 qg + 7 of each k-step
+  const int col = lane & 15, qg = lane >> 4;
+  uint4 qf[D / 32];
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    qf[s] = uint4{0u, 0u, 0u, 0u};
+    if (col < gw) {
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(q + (static_cast<int64_t>(b) * Hq + h0 + col) * D + 32 * s + 8 * qg);
+      qf[s] = uint4{src[0], src[1], src[2], src[3]};
+    }
   }
+  // output: o[t][u] holds value column 16 t + 4 qg + u of head col (the
+  // transposed product's accumulator layout)
+  constexpr int kTiles = D / 16;
+  f32x4 o[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;   // head col, the same in the four lane groups
+
   const int64_t row0 = (static_cast<int64_t>(b) * Hkv + kv) * S;   // cache row of position 0
-  constexpr int kPieces = D / 8;                                     // 16-byte pieces per row
-  constexpr int kLoads = kAtSub * kPieces / kAtThreads;              // per thread and step, each of K and V
-
-  // score roles: lane = position within the step, wave w = query slots 2w and 2w + 1
-  const int ga = 2 * wave, gb = 2 * wave + 1;
-  const bool use_a = ga < gw, use_b = gb < gw;
-  float m_a = -INFINITY, m_b = -INFINITY, l_a = 0.f, l_b = 0.f;
-
-  // value roles: lane = (8-column block cb, slot group hgp); wave w takes positions w, w + 4, ...
-  constexpr int kCB = D / 8;
-  constexpr int kHG = 64 / kCB;      // 2, 4 or 8 slot groups
-  constexpr int kHPT = kAtGroup / kHG;   // 4, 2 or 1 slots per lane
-  const int cb = lane % kCB, hgp = lane / kCB;
-  float acc[kHPT][8];
+  const i32x4 krs = buffer_rsrc(kc + row0 * D), vrs = buffer_rsrc(vc + row0 * D);
+  const uint32_t kslot = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr(&sm.kv[wave][0][0]))));
+  const uint32_t vslot = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_addr(&sm.kv[wave][1][0]))));
+  // byte offsets (from the head's position 0) of this lane's 16-byte pieces of
+  // a stage at p0; rows past the range re-read its last row
+  uint32_t off[G::kLoads];
+  auto offsets = [&](int p0) {
 #pragma unroll
-  for (int j = 0; j < kHPT; ++j)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[j][c] = 0.f;
-
-  // next step's rows, loaded into registers while the current step computes
-  uint4 kr[kLoads], vr[kLoads];
-  auto load_step = [&](int p0) {
-    const int n = min(kAtSub, end - p0);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int idx = tid + i * kAtThreads;
-      const int r = idx / kPieces, c = idx % kPieces;
-      kr[i] = vr[i] = uint4{0u, 0u, 0u, 0u};
-      if (r < n) {
-        const int64_t off = (row0 + p0 + r) * D + c * 8;
-        kr[i] = *reinterpret_cast<const uint4*>(kc + off);
-        vr[i] = *reinterpret_cast<const uint4*>(vc + off);
-      }
+    for (int j = 0; j < G::kLoads; ++j) {
+      const int byte = j * 1024 + lane * 16;
+      const int r = byte / G::kRowBytes, ph = (byte % G::kRowBytes) / 16;
+      const int p = min(p0 + r, end - 1);
+      off[j] = static_cast<uint32_t>((p * D + at_chunk<D>(r, ph) * 8) * 2);
     }
   };
-  load_step(start);
+  auto issue = [&](const i32x4& rs, uint32_t slot) {
+#pragma unroll
+    for (int j = 0; j < G::kLoads; ++j) bdma16(rs, off[j], 0u, slot + j * 1024);
+  };
+  const unsigned char* ks = &sm.kv[wave][0][0];
+  const unsigned char* vs = &sm.kv[wave][1][0];
 
-  for (int p0 = start; p0 < end; p0 += kAtSub) {
-    const int n = min(kAtSub, end - p0);
-    __syncthreads();   // the previous step's reads of k, v, p and alpha are done
+  if (my_st > 0) {
+    offsets(start + wave * kAtPos);
+    issue(krs, kslot);
+    issue(vrs, vslot);
+  }
+  for (int i = 0; i < my_st; ++i) {
+    const int p0 = start + (wave + i * kAtWaves) * kAtPos;
+    const int nv = min(kAtPos, end - p0);
+    const bool more = i + 1 < my_st;
+    wait_vmcnt<G::kLoads>();   // this stage's keys (its values may still be in flight)
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int idx = tid + i * kAtThreads;
-      const int r = idx / kPieces, c = idx % kPieces;
-      *reinterpret_cast<uint4*>(&sm.k[r][c * 8]) = kr[i];
-      *reinterpret_cast<uint4*>(&sm.v[r][c * 8]) = vr[i];
+    for (int s = 0; s < D / 32; ++s) {
+      const bf16x8 kf =
+          *reinterpret_cast<const bf16x8*>(ks + col * G::kRowBytes + at_chunk<D>(col, 4 * s + qg) * 16);
+      sc = mfma16(kf, __builtin_bit_cast(bf16x8, qf[s]), sc);
     }
-    __syncthreads();
-    if (p0 + kAtSub < end) load_step(p0 + kAtSub);
-
-    // lane = (position lane % 32, slot 2w + lane / 32): one dot product per lane
-    const int pos = lane & 31, g = 2 * wave + (lane >> 5);
-    if (use_a) {   // wave-uniform
-      float sa = 0.f;
-      const uint16_t* krow = &sm.k[pos][0];
-#pragma unroll 4
-      for (int d = 0; d < D; d += 8)
-        sa = dot8(*reinterpret_cast<const uint4*>(&sm.q[g][d / 2]), *reinterpret_cast<const uint4*>(krow + d), sa);
-      const bool live = pos < n;
-      const float sc = live ? sa * scale : -INFINITY;
-      float mx = sc;
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float mo = (lane >> 5) ? m_b : m_a;
-      const float mn = fmaxf(mo, mx);   // finite: position 0 is live
-      const float al = expf(mo - mn);
-      const float e = live ? expf(sc - mn) : 0.f;
-      float es = e;
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) es += __shfl_xor(es, o);
-      // both halves' running values, kept in every lane
-      const float al_a = __shfl(al, 0), al_b = __shfl(al, 32);
-      const float es_a = __shfl(es, 0), es_b = __shfl(es, 32);
-      const float mn_a = __shfl(mn, 0), mn_b = __shfl(mn, 32);
-      l_a = l_a * al_a + es_a;
-      m_a = mn_a;
-      if (use_b) {
-        l_b = l_b * al_b + es_b;
-        m_b = mn_b;
-      }
-      if (g < gw) {
-        sm.p[pos][g] = e;
-        if (pos == 0) sm.alpha[g] = al;
-      }
+    // sc[u]: position 4 qg + u of the stage, head col
+    wait_lgkm0();
+    if (more) {
+      offsets(p0 + kAtWaves * kAtPos);
+      issue(krs, kslot);
     }
-    __syncthreads();
-
+    float sv[4], mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kHPT; ++j) {
-      const int g = hgp * kHPT + j;
-      const float al = g < gw ? sm.alpha[g] : 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[j][c] *= al;
+    for (int u = 0; u < 4; ++u) {
+      sv[u] = 4 * qg + u < nv ? sc[u] * scale : -INFINITY;
+      mx = fmaxf(mx, sv[u]);
     }
-    for (int r = wave; r < n; r += 4) {
-      float vf[8];
-      const uint4 w = *reinterpret_cast<const uint4*>(&sm.v[r][cb * 8]);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m_run, mx);   // finite: the stage's first position is live
+    const float al = expf(m_run - mn);
+    float ev[4], es = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vf[2 * i] = __uint_as_float(u[i] << 16);
-        vf[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-      }
-      float pr[kHPT];
-      if constexpr (kHPT == 4) {
-        const float4 t = *reinterpret_cast<const float4*>(&sm.p[r][hgp * 4]);
-        pr[0] = t.x; pr[1] = t.y; pr[2] = t.z; pr[3] = t.w;
-      } else if constexpr (kHPT == 2) {
-        const float2 t = *reinterpret_cast<const float2*>(&sm.p[r][hgp * 2]);
-        pr[0] = t.x; pr[1] = t.y;
-      } else {
-        pr[0] = sm.p[r][hgp];
-      }
-#pragma unroll
-      for (int j = 0; j < kHPT; ++j)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[j][c] = fmaf(pr[j], vf[c], acc[j][c]);
+    for (int u = 0; u < 4; ++u) {
+      ev[u] = 4 * qg + u < nv ? expf(sv[u] - mn) : 0.f;
+      es += ev[u];
     }
+    es += __shfl_xor(es, 16);
+    es += __shfl_xor(es, 32);
+    l_run = l_run * al + es;
+    m_run = mn;
+    // probabilities as the second operand (positions 4 qg .. 4 qg + 3 of head
+    // col): high bf16 part and the bf16 remainder (both exact splits of the
+    // fp32 value up to the remainder's own rounding)
+    bf16x4 phi, plo;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint16_t h = f32_to_bf16_bits(ev[u]);
+      const float hv = __uint_as_float(static_cast<uint32_t>(h) << 16);
+      phi[u] = static_cast<short>(h);
+      plo[u] = static_cast<short>(f32_to_bf16_bits(ev[u] - hv));
+    }
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) o[t] *= al;
+    if (more)
+      wait_vmcnt<G::kLoads>();   // this stage's values (the next keys may still be in flight)
+    else
+      wait_vmcnt<0>();
+    // first operand: value column 16 t + col at positions 4 qg .. 4 qg + 3
+    const int vc8 = col >> 3, ve = (col & 7) * 2;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      bf16x4 va;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * qg + u;
+        va[u] = *reinterpret_cast<const short*>(vs + r * G::kRowBytes + at_chunk<D>(r, 2 * t + vc8) * 16 + ve);
+      }
+      o[t] = mfma16k16(va, phi, o[t]);
+      o[t] = mfma16k16(va, plo, o[t]);
+    }
+    wait_lgkm0();
+    if (more) issue(vrs, vslot);
   }
 
-  // the four waves' partial sums, added in wave order, through the key and value area
+  // the waves' states, combined in wave order through their own slots
   __syncthreads();
-  float* red = reinterpret_cast<float*>(&sm.k[0][0]);   // [4][64][kHPT * 8]
-  static_assert(4 * 64 * kHPT * 8 * sizeof(float) <= sizeof(sm.k) + sizeof(sm.v), "reduction buffer");
-#pragma unroll
-  for (int j = 0; j < kHPT; ++j)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) red[(wave * 64 + lane) * (kHPT * 8) + j * 8 + c] = acc[j][c];
-  __syncthreads();
-  for (int o = tid; o < kAtGroup * D; o += kAtThreads) {
-    const int g = o / D, d = o % D;
-    if (g >= gw) continue;
-    const int ln = (g / kHPT) * kCB + d / 8, slot = (g % kHPT) * 8 + d % 8;
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) sum += red[(w * 64 + ln) * (kHPT * 8) + slot];
-    part_o[((static_cast<int64_t>(b) * Hq + h0 + g) * n_splits + split) * D + d] = sum;
+  float* mine = reinterpret_cast<float*>(&sm.kv[wave][0][0]);   // m [8], l [8], o [8][D]
+  static_assert((2 * kAtGroup + kAtGroup * D) * sizeof(float) <= 2 * AtGeom<D>::kSlot, "state area");
+  if (qg == 0 && col < kAtGroup) {
+    mine[col] = m_run;
+    mine[kAtGroup + col] = l_run;
   }
-  if (lane == 0) {
-    if (use_a) {
-      float* ml = part_ml + ((static_cast<int64_t>(b) * Hq + h0 + ga) * n_splits + split) * 2;
-      ml[0] = m_a;
-      ml[1] = l_a;
+  if (col < kAtGroup) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+      *reinterpret_cast<f32x4*>(mine + 2 * kAtGroup + col * D + 16 * t + 4 * qg) = o[t];
+  }
+  __syncthreads();
+  // per head: the range's maximum M, each wave's factor e^(m_w - M) (0 for a
+  // wave with no stage, m = -inf) and the range's sum
+  float* fac = &sm.fac[0][0];
+  if (tid < kAtGroup) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAtWaves; ++w) M = fmaxf(M, reinterpret_cast<const float*>(&sm.kv[w][0][0])[tid]);
+    float den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAtWaves; ++w) {
+      const float* st = reinterpret_cast<const float*>(&sm.kv[w][0][0]);
+      const float f = expf(st[tid] - M);
+      fac[tid * kAtWaves + w] = f;
+      den = fmaf(f, st[kAtGroup + tid], den);
     }
-    if (use_b) {
-      float* ml = part_ml + ((static_cast<int64_t>(b) * Hq + h0 + gb) * n_splits + split) * 2;
-      ml[0] = m_b;
-      ml[1] = l_b;
+    if (tid < gw) {
+      float* ml = part_ml + ((static_cast<int64_t>(b) * Hq + h0 + tid) * n_splits + split) * 2;
+      ml[0] = M;
+      ml[1] = den;
     }
+  }
+  __syncthreads();
+  for (int i = tid; i < gw * D; i += kAtThreads) {
+    const int g = i / D, d = i % D;
+    float num = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAtWaves; ++w)
+      num = fmaf(fac[g * kAtWaves + w], reinterpret_cast<const float*>(&sm.kv[w][0][0])[2 * kAtGroup + g * D + d],
+                 num);
+    part_o[((static_cast<int64_t>(b) * Hq + h0 + g) * n_splits + split) * D + d] = num;
   }
 }
 
@@ -306,13 +351,14 @@ __global__ __launch_bounds__(kMgThreads) void k_gqa_merge(const float* __restric
 }  // namespace
 
 GqaPlan gqa_plan(int B, int Hq, int Hkv, int S, bool packed) {
+  constexpr int kBlock = kAtWaves * kAtPos;   // one stage per wave
   const int per_wg = packed ? Hq / Hkv : 1;
-  const int64_t steps = static_cast<int64_t>(B) * (Hq / per_wg) * div_up(S, kAtSub);
-  int64_t nsub = steps / kAtTarget;
-  nsub = nsub < 1 ? 1 : (nsub > 16 ? 16 : nsub);
+  const int64_t blocks = static_cast<int64_t>(B) * (Hq / per_wg) * div_up(S, kBlock);
+  int64_t nsub = blocks / kAtTarget;
+  nsub = nsub < 1 ? 1 : (nsub > 64 ? 64 : nsub);
   GqaPlan p;
   p.heads_per_wg = per_wg;
-  p.rows_per_split = static_cast<int>(nsub) * kAtSub;
+  p.rows_per_split = static_cast<int>(nsub) * kBlock;
   p.n_splits = static_cast<int>(div_up(S, p.rows_per_split));
   return p;
 }

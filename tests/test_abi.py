@@ -245,8 +245,10 @@ def test_host_routing_checks(m):
 
 def test_gqa_workspace_and_checks(m):
     L = m.lib()
-    # 32768 positions, 2 key/value heads: 1024 steps of 64 -> 2 per range, 256 ranges
-    assert L.moe_gqa_decode_workspace_bytes(1, 16, 2, 256, 32768) == 16 * 256 * (256 + 2) * 4
+    # 32768 positions, 2 key/value heads: 256 blocks of 128 positions (a
+    # 16-position stage per wave of 8) per head -> 1 block per range, 256
+    # workgroups, 128 ranges per head
+    assert L.moe_gqa_decode_workspace_bytes(1, 16, 2, 256, 32768) == 16 * 128 * (256 + 2) * 4
     assert L.moe_gqa_decode_workspace_bytes(1, 16, 2, 96, 100) == 0          # head_dim
     assert L.moe_gqa_decode_workspace_bytes(1, 18, 2, 128, 100) == 0         # 9 query heads per group
     need = L.moe_gqa_decode_workspace_bytes(2, 16, 2, 128, 1000)
