@@ -309,9 +309,12 @@ def test_forward_parity_full(dname, T):
 # hidden 512 / inter 256 / shared 384: the fewest K blocks the one-workgroup-per-CU
 # GEMM takes (4), a shared expert wider than the routed ones (routed gate/up
 # slices past the routed width are skipped) and more than one tile per
-# workgroup; hidden 320 takes the one-tile-per-workgroup GEMM (odd K blocks)
+# workgroup; hidden 320 takes the one-tile-per-workgroup GEMM (odd K blocks).
+# 16 experts at T = 16384 and 128 experts at T = 8192: expert counts below and
+# between the router's 64-expert tiles, 65536 routed slots each
 @pytest.mark.parametrize("hidden,inter,shared,E,k,T", [(512, 256, 384, 64, 6, 300), (512, 256, 384, 64, 6, 2000),
-                                                         (320, 256, 128, 32, 4, 500)])
+                                                         (320, 256, 128, 32, 4, 500), (256, 128, 128, 16, 4, 16384),
+                                                         (512, 128, 128, 128, 8, 8192)])
 def test_forward_parity_gemm_forms(hidden, inter, shared, E, k, T):
     d = synth.Dims(hidden=hidden, inter=inter, n_experts=E, top_k=k, group_size=64, shared_inter=shared)
     say("forward gemm forms", d, T)
