@@ -346,8 +346,9 @@ moe_status moe_forward_host_routing(const moe_dims* d, const moe_layer* layer, c
  *   in use (values are clamped to [0, S]); out [B][Hq][D] bf16.
  *   Query head h reads key/value head h / (Hq / Hkv):
  *   out = sum_p softmax_p(scale * q . k_p) v_p over p < seq_lens[b], scores,
- *   softmax and sums in fp32, one bf16 rounding; a sequence of length 0 gives
- *   zeros.  The positions are cut into ranges that run in parallel; their
+ *   softmax and sums in fp32 (the probabilities enter the weighted sum of
+ *   value rows split into two bf16 parts, 16 significant bits), one bf16
+ *   rounding; a sequence of length 0 gives zeros.  The positions are cut into ranges that run in parallel; their
  *   partial results are merged in range order, so out is reproducible.
  *   pack_heads = 1: a workgroup takes all Hq / Hkv query heads of a group and
  *   loads each key/value row once; pack_heads = 0: one query head per
