@@ -527,6 +527,31 @@ def test_forward_repeatable():
         assert torch.equal(y, outs[0][1])      # fixed-order combine: bitwise reproducible
 
 
+@pytest.mark.parametrize("T", [1, 3, 300])
+def test_forward_stages_compose(T):
+    """moe_forward_stages run one stage at a time, in order, on a fresh
+    workspace gives moe_forward's outputs bit for bit (the per-stage timing of
+    the bench relies on it); the fused forms run whole in the router stage."""
+    say("forward stages compose T", T)
+    m = gu.moe()
+    d = MODEL
+    lay = synth.make_layer(d, 91 + T)
+    dl = gu.device_layer(lay, d)
+    md = gu.to_dims(d)
+    x = synth.activations(T, d.hidden, 91 + T).cuda()
+    ref_ids = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
+    ref = m.moe_forward(md, dl, x, ids_out=ref_ids)
+    ws = m.moe_workspace(md, T)
+    y = torch.empty((T, d.hidden), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, d.top_k), dtype=torch.int32, device="cuda")
+    for st in range(len(m.STAGES)):
+        m.moe_forward_stages(md, dl, x, y, ws, st, st, ids_out=ids)
+    torch.cuda.synchronize()
+    assert m.moe_workspace_errors(ws) == 0
+    assert torch.equal(ids, ref_ids)
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
 @pytest.mark.parametrize("T", [1, 300])
 def test_graph_capture_replays(T):
     """The layer makes no host round trip: it captures into a HIP graph, and
