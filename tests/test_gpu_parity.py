@@ -311,10 +311,13 @@ def test_forward_parity_full(dname, T):
 # slices past the routed width are skipped) and more than one tile per
 # workgroup; hidden 320 takes the one-tile-per-workgroup GEMM (odd K blocks).
 # 16 experts at T = 16384 and 128 experts at T = 8192: expert counts below and
-# between the router's 64-expert tiles, 65536 routed slots each
+# between the router's 64-expert tiles, 65536 routed slots each.  k = 16 and
+# k = 1 over 256 experts: the general top-k and the combine with k known only
+# at run time
 @pytest.mark.parametrize("hidden,inter,shared,E,k,T", [(512, 256, 384, 64, 6, 300), (512, 256, 384, 64, 6, 2000),
                                                          (320, 256, 128, 32, 4, 500), (256, 128, 128, 16, 4, 16384),
-                                                         (512, 128, 128, 128, 8, 8192)])
+                                                         (512, 128, 128, 128, 8, 8192), (512, 256, 256, 256, 16, 200),
+                                                         (512, 256, 256, 256, 1, 300)])
 def test_forward_parity_gemm_forms(hidden, inter, shared, E, k, T):
     d = synth.Dims(hidden=hidden, inter=inter, n_experts=E, top_k=k, group_size=64, shared_inter=shared)
     say("forward gemm forms", d, T)
