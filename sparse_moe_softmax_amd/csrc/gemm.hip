@@ -170,6 +170,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
   constexpr int kAStage = Ring<MT, KS>::kA;        // stage layout: A of each K block, then B of each
   constexpr int kBOff = KS * kAStage;
   static_assert((kStages - 2) * kDma <= 63, "vmcnt range");
+  // Where an iteration issues the next stage's loads: the down GEMMs (8 K
+  // blocks a tile) issue them right after the first MFMAs of the iteration,
+  // so the matrix core starts sooner after the barrier; the gate/up GEMM
+  // issues them right after the barrier (it measured slower the other way).
+  constexpr bool kLateIssue = MODE != kSwiglu;
   const int wave = t.wave, lane = t.lane;
   const int col = lane & 31, gq = lane >> 5;
 
@@ -287,7 +292,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
     else
       wait_stages<kDma, kStages - 2>(min(kStages - 2, kg - 1 - kb));
     __builtin_amdgcn_s_barrier();   // stage kb landed for every wave; stage kb-1 consumed
-    if (kSteady || kb + kStages - 1 < kg) issue(kb + kStages - 1);
+    const bool do_issue = kSteady || kb + kStages - 1 < kg;
+    if (!kLateIssue && do_issue) issue(kb + kStages - 1);
     const unsigned char* st = ring + (kb % kStages) * kStageBytes;
     BRaw raw[KS];
 #pragma unroll
@@ -312,6 +318,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m][c] = mma<MODE>(af[q & 1][m], bq[q & 1][c], acc[m][c]);
+        if (kLateIssue && q == 0 && c == 0 && do_issue) issue(kb + kStages - 1);
         if (q + 1 < 4 * KS) bq[(q + 1) & 1][c] = dq(raw[nu], c, nks);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -334,7 +341,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
     BRaw raw;
     if (more) read_b(kb + 1, 0, raw);   // this wave's own loads: no barrier needed
     __builtin_amdgcn_s_barrier();    // stage kb+1 landed for every wave; stage kb-1 consumed
-    if (kSteady || kb + kStages - 1 < kg) issue(kb + kStages - 1);
+    const bool do_issue = kSteady || kb + kStages - 1 < kg;
+    if (!kLateIssue && do_issue) issue(kb + kStages - 1);
     const unsigned char* st = ring + (kb % kStages) * kStageBytes;
     const unsigned char* st_next = ring + ((kb + 1) % kStages) * kStageBytes;
 #pragma unroll
@@ -347,6 +355,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& t, unsi
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m][c] = mma<MODE>(af[ks & 1][m], bcur[c][ks], acc[m][c]);
+        if (kLateIssue && ks == 0 && c == 0 && do_issue) issue(kb + kStages - 1);
         if (more) bnext[c][ks] = dq(raw, c, ks);
         __builtin_amdgcn_sched_barrier(0);
       }
