@@ -169,7 +169,8 @@ def _ids(T, E, k, mode, seed):
 @pytest.mark.parametrize("T,E,k,bm,mode", [
     (1, 256, 8, 128, "uniform"), (64, 256, 8, 128, "uniform"), (65, 256, 8, 16, "uniform"),
     (512, 256, 8, 128, "uniform"), (4096, 256, 8, 128, "uniform"), (16384, 256, 8, 128, "zipf"),
-    (200, 16, 4, 7, "one_hot"), (1000, 256, 8, 1, "zipf"), (129, 64, 16, 64, "uniform")])
+    (200, 16, 4, 7, "one_hot"), (1000, 256, 8, 1, "zipf"), (129, 64, 16, 64, "uniform"),
+    (1024, 256, 8, 128, "zipf"), (1040, 256, 8, 128, "zipf")])   # the last one-launch size and the next
 def test_group_bit_exact(T, E, k, bm, mode):
     say("group T E k bm mode", T, E, k, bm, mode)
     m = gu.moe()
