@@ -1,10 +1,11 @@
-"""Codegen guard for the grouped GEMM (CPU only: cross-compiles for gfx950).
+"""Codegen guard for the grouped GEMM and the router GEMM (CPU only:
+cross-compiles for gfx950).
 
 The K loop waits for its direct-to-LDS loads with explicit vmcnt counts, which
 is only correct if those loads are the only vector-memory instructions inside
 the loop (no compiler loads, stores or register spills to scratch).  This test
-compiles gemm.hip to gfx950 assembly and checks exactly that for every K loop,
-and that the steady-state loops are single basic blocks.
+compiles gemm.hip and route.hip to gfx950 assembly and checks exactly that for
+every K loop.
 """
 
 import os
@@ -20,14 +21,18 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.mark.skipif(shutil.which("/opt/rocm/bin/hipcc") is None and shutil.which("hipcc") is None,
                     reason="hipcc not available")
-def test_k_loops_issue_only_direct_lds_loads(tmp_path):
+@pytest.mark.parametrize("src,pattern,count,min_loops", [
+    ("gemm.hip", r"^(_ZN3moe9k_gemm_q4ILi\dEEEvNS_8GemmArgsE):", 3, 2),
+    ("route.hip", r"^(_ZN3moe\d+k_router_gemm\w*EPKtS1_PKfS3_iiiiPfS4_):", 2, 1),
+])
+def test_k_loops_issue_only_direct_lds_loads(tmp_path, src, pattern, count, min_loops):
     from sparse_moe_softmax_amd import build as B
-    asm = tmp_path / "gemm.s"
-    cmd = [B.HIPCC, *B.FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, "gemm.hip"), "-o", str(asm)]
+    asm = tmp_path / (src + ".s")
+    cmd = [B.HIPCC, *B.FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(asm)]
     subprocess.run(cmd, check=True, capture_output=True)
     s = asm.read_text()
-    kernels = re.findall(r"^(_ZN3moe9k_gemm_q4ILi\dEEEvNS_8GemmArgsE):", s, re.M)
-    assert len(kernels) == 3
+    kernels = re.findall(pattern, s, re.M)
+    assert len(kernels) == count
     assert "scratch_" not in s, "register spills to scratch memory"
     for k in kernels:
         a = s.index(k + ":")
@@ -48,7 +53,7 @@ def test_k_loops_issue_only_direct_lds_loads(tmp_path):
             if cur and re.match(r"(global_|buffer_|scratch_|flat_)", op):
                 ops[cur].append("lds-load" if re.match(r"(global|buffer)_load_\w+ .* lds$", text) else text)
         k_loops = {h: v for h, v in ops.items() if "lds-load" in v}
-        assert len(k_loops) >= 2, k
+        assert len(k_loops) >= min_loops, k
         for h, v in k_loops.items():
             others = [o for o in v if o != "lds-load"]
             assert not others, (k, h, others)
