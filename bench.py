@@ -605,7 +605,7 @@ def main():
                     help="decode steps the oracle's 40-layer decode timing covers (scaled to 256)")
     ap.add_argument("--profile-stage", default=None,
                     help="profiling run: one stage repeated, no JSON line (gqa_decode: the attention leg alone; "
-                         "decode: the 40-layer decode leg alone)")
+                         "decode: the 40-layer decode leg alone; small_t: the 8- and 16-token layers alone)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -635,6 +635,10 @@ def main():
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
+        return
+    if args.profile_stage == "small_t":
+        # the 8- and 16-token points of the small-batch sweep alone (args.steps graph replays each)
+        print(json.dumps({"small_t": bench_small_t(synth.CONFIGS["decode"], Ts=(8, 16), reps=args.steps)}), flush=True)
         return
     if args.profile_stage:
         profile_stage(cfg, args.profile_stage, args.steps)
