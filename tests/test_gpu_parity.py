@@ -531,7 +531,7 @@ def test_forward_repeatable():
         assert torch.equal(y, outs[0][1])      # fixed-order combine: bitwise reproducible
 
 
-@pytest.mark.parametrize("T", [1, 3, 300])
+@pytest.mark.parametrize("T", [1, 3, 300, 2048])
 def test_forward_stages_compose(T):
     """moe_forward_stages run one stage at a time, in order, on a fresh
     workspace gives moe_forward's outputs bit for bit (the per-stage timing of
@@ -556,11 +556,13 @@ def test_forward_stages_compose(T):
     assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("T", [1, 300])
+@pytest.mark.parametrize("T", [1, 300, 2048])
 def test_graph_capture_replays(T):
     """The layer makes no host round trip: it captures into a HIP graph, and
     every replay (with unrelated eager work and synchronisations between
-    replays) reproduces the eager result."""
+    replays) reproduces the eager result.  T = 1: the fused layer; 300: the
+    one-launch grouping; 2048: the two-launch grouping (more than 64 routing
+    tiles)."""
     say("graph capture T", T)
     m = gu.moe()
     d = MODEL
