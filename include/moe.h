@@ -17,6 +17,8 @@
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The library
  *     allocates no device memory and keeps no device state between calls; the
  *     caller provides scratch memory as `workspace` where a call needs it.
+ *     The one exception is moe_forward_noalloc(), whose scratch is a device
+ *     array of the library itself (see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls enqueue their kernels on it and return without synchronising the
  *     host; results are ready when the stream reaches that point.
