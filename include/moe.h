@@ -149,7 +149,7 @@ moe_status moe_prepack_router(const moe_dims* d, const float* router_w, uint16_t
 moe_status moe_router_logits(const moe_dims* d, const moe_layer* layer, const uint16_t* x, int32_t T,
                              float* logits, float* shared_logit, void* stream);
 
-/* Top-k routing from logits ("... and picks 8", same section).
+/* Top-k routing from logits: each token keeps its 8 best-scored experts (same section).
  *   logits [T][E] fp32 -> ids [T][k] int32: the k largest logits in descending
  *   order, equal logits (+0 == -0) ordered by the lower expert index;
  *   weights [T][k] fp32: softmax over all E logits restricted to the kept
