@@ -1,6 +1,6 @@
 // Grouped expert GEMMs with int4 weights dequantised in registers.  The
-// method rebuilds the 4-bit weights one tile at a time inside the grouped GEMM,
-// so the expanded values exist only in registers and are never written back
+// method expands the quantised weights inside the grouped GEMM, a tile per
+// step, so the expanded values exist only in registers and are never written back
 // (Inside Lily page, section "Performance Gains and Workload Patterns"); prefill
 // is matrix-matrix work for the matrix units (Lily page, section "Why Apple
 // Silicon isn't just a smaller datacenter GPU").
