@@ -6,8 +6,8 @@
 //
 // What it computes (the pages: "Lily: Perplexity's Custom Inference Engine for
 // Apple Silicon", section "The architecture that forces the issue: MoE plus
-// Gated DeltaNet" -- a router scores 256 experts and picks 8, plus a shared
-// expert that every token runs through; "Inside Lily ...", section "Performance
+// Gated DeltaNet" -- each token is scored against 256 experts, keeps the best
+// eight, and also passes through one shared expert; "Inside Lily ...", section "Performance
 // Gains and Workload Patterns" -- 4-bit weights rebuilt tile by tile inside the
 // grouped GEMM, routing histograms and block maps kept on the GPU).  The pages
 // give no formulas; the precise definition used here (softmax over the router
