@@ -2,8 +2,9 @@
 """Benchmark of the sparse-MoE layer on one MI355X.
 
 One step = one whole MoE layer (router GEMM, top-k, grouping, gate/up grouped
-GEMM with SwiGLU, down grouped GEMM with weighted scatter, combine) over one
-batch of T synthetic tokens, inputs and weights resident in HBM.
+GEMM with SwiGLU, down grouped GEMM writing each slot's output, weighted
+combine) over one batch of T synthetic tokens, inputs and weights resident in
+HBM.
 
 Headline (``value``): prefill tokens/s of one layer at T=4096 (hidden 2048,
 256 experts top-8 + 1 shared expert, expert intermediate 512, int4 group-64
