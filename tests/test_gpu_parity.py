@@ -170,7 +170,8 @@ def _ids(T, E, k, mode, seed):
     (1, 256, 8, 128, "uniform"), (64, 256, 8, 128, "uniform"), (65, 256, 8, 16, "uniform"),
     (512, 256, 8, 128, "uniform"), (4096, 256, 8, 128, "uniform"), (16384, 256, 8, 128, "zipf"),
     (200, 16, 4, 7, "one_hot"), (1000, 256, 8, 1, "zipf"), (129, 64, 16, 64, "uniform"),
-    (1024, 256, 8, 128, "zipf"), (1040, 256, 8, 128, "zipf")])   # the last one-launch size and the next
+    (1024, 256, 8, 128, "zipf"), (1040, 256, 8, 128, "zipf"),   # the last one-launch size and the next
+    (2000, 256, 8, 4096, "zipf"), (300, 32, 8, 4096, "uniform")])   # the largest tile height moe_group takes
 def test_group_bit_exact(T, E, k, bm, mode):
     say("group T E k bm mode", T, E, k, bm, mode)
     m = gu.moe()
